@@ -1,0 +1,351 @@
+// C ABI of libeagle3_attn.so: argument validation, share geometry (the shard
+// driver) and kernel launches. Declarations and the contract are in
+// include/eagle3_attn.h.
+#include "eagle3_attn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "e3_common.h"
+
+namespace e3 {
+hipError_t launch_fwd(const Args& a, int dtype, int D, hipStream_t st);
+hipError_t launch_bwd(const Args& a, int dtype, int D, hipStream_t st);
+hipError_t launch_lse_merge(float* out, float* lse, const float* bo, const float* bl, int B, int T,
+                            int H, int D, int blayout, hipStream_t st);
+int fwd_tile_rows();
+int fwd_tile_keys();
+}  // namespace e3
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return E3_OK;
+}
+
+struct Resolved {
+  int N;
+  long long k0_bs, kd_bs, kd_blk;
+  int ndocs;
+};
+
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+// Validates a problem; fills the resolved strides. `whole` restricts the layout to
+// the full-sequence entry points (FULL or HEADSHARD).
+int validate(const e3_problem* p, Resolved& r, bool whole, bool need_dev = true) {
+  if (!p) return fail(E3_EINVAL, "problem is NULL");
+  if (p->dtype != E3_BF16 && p->dtype != E3_F32) return fail(E3_EINVAL, "dtype %d is not E3_BF16 or E3_F32", p->dtype);
+  if (p->D != 64 && p->D != 128) return fail(E3_EUNSUPPORTED, "head dim D=%d (supported: 64, 128)", p->D);
+  if (p->B < 1) return fail(E3_EINVAL, "B=%d must be >= 1", p->B);
+  if (p->H < 1) return fail(E3_EINVAL, "H=%d must be >= 1", p->H);
+  if (p->T < 0 || p->T_kv < 0) return fail(E3_EINVAL, "T=%d, T_kv=%d must be >= 0", p->T, p->T_kv);
+  if (p->num_blocks < 1 || p->num_blocks > 16)
+    return fail(E3_EINVAL, "num_blocks=%d must be in [1, 16]", p->num_blocks);
+  if (!(std::isfinite(p->scale) && p->scale > 0.f)) return fail(E3_EINVAL, "scale must be finite and > 0");
+  const long long T = p->T, Tkv = p->T_kv;
+  switch (p->layout) {
+    case E3_LAYOUT_FULL:
+      if (p->cp != 1 || p->rank != 0) return fail(E3_EINVAL, "FULL layout needs cp=1, rank=0");
+      if (Tkv != T) return fail(E3_EINVAL, "FULL layout needs T_kv == T (%lld vs %lld)", Tkv, T);
+      break;
+    case E3_LAYOUT_HEADSHARD:
+      if (p->cp < 1 || p->rank < 0 || p->rank >= p->cp) return fail(E3_EINVAL, "bad cp=%d / rank=%d", p->cp, p->rank);
+      if (Tkv != T) return fail(E3_EINVAL, "HEADSHARD layout needs T_kv == T (%lld vs %lld)", Tkv, T);
+      if (T % p->cp != 0)
+        return fail(E3_EINVAL, "HEADSHARD: sequence length %lld must divide by the Ulysses degree %d", T, p->cp);
+      break;
+    case E3_LAYOUT_CONTIGUOUS:
+      if (p->cp < 1 || p->rank < 0 || p->rank >= p->cp) return fail(E3_EINVAL, "bad cp=%d / rank=%d", p->cp, p->rank);
+      if (Tkv != (long long)p->cp * T) return fail(E3_EINVAL, "CONTIGUOUS layout needs T_kv == cp*T");
+      break;
+    case E3_LAYOUT_ZIGZAG:
+      if (p->cp < 1 || p->rank < 0 || p->rank >= p->cp) return fail(E3_EINVAL, "bad cp=%d / rank=%d", p->cp, p->rank);
+      if (T % 2 != 0) return fail(E3_EINVAL, "ZIGZAG layout needs an even local length (two chunks), T=%lld", T);
+      if (Tkv != (long long)p->cp * T) return fail(E3_EINVAL, "ZIGZAG layout needs T_kv == cp*T");
+      if (p->B != 1) return fail(E3_EINVAL, "ZIGZAG layout is varlen and unbatched: B must be 1");
+      break;
+    default:
+      return fail(E3_EINVAL, "unknown layout %d", p->layout);
+  }
+  if (whole && p->layout != E3_LAYOUT_FULL && p->layout != E3_LAYOUT_HEADSHARD)
+    return fail(E3_EINVAL, "eagle3_attn_fwd/bwd take the FULL or HEADSHARD layout; use eagle3_shard_fwd/bwd");
+  if (Tkv > 0x3fffffffLL) return fail(E3_EUNSUPPORTED, "sequence length %lld too large", Tkv);
+  if (p->num_docs < 0) return fail(E3_EINVAL, "num_docs=%d must be >= 0", p->num_docs);
+  r.ndocs = p->num_docs;
+  if (p->num_docs >= 1) {
+    const int32_t* cu = p->cu_seqlens_host;
+    if (!cu) return fail(E3_EINVAL, "cu_seqlens_host is NULL with num_docs=%d", p->num_docs);
+    if (cu[0] != 0) return fail(E3_EINVAL, "cu_seqlens[0]=%d must be 0", cu[0]);
+    for (int i = 0; i < p->num_docs; ++i)
+      if (cu[i + 1] < cu[i]) return fail(E3_EINVAL, "cu_seqlens must be non-decreasing (index %d)", i + 1);
+    if (cu[p->num_docs] != Tkv)
+      return fail(E3_EINVAL, "cu_seqlens ends at %d, the sequence length is %lld", cu[p->num_docs], Tkv);
+    if (p->num_docs > 1) {
+      if (p->B != 1) return fail(E3_EINVAL, "several documents (varlen) need B == 1");
+      if (p->layout == E3_LAYOUT_ZIGZAG)
+        return fail(E3_EUNSUPPORTED, "several documents with the ZIGZAG layout (per-document halving) are not supported");
+      if (need_dev && !p->cu_seqlens_dev)
+        return fail(E3_EINVAL, "cu_seqlens_dev is NULL with num_docs=%d", p->num_docs);
+    }
+  }
+  r.N = p->num_blocks - 1;
+  const long long HD = (long long)p->H * p->D;
+  r.k0_bs = p->k0_batch_stride ? p->k0_batch_stride : Tkv * HD;
+  r.kd_blk = p->kd_block_stride ? p->kd_block_stride : T * HD;
+  r.kd_bs = p->kd_batch_stride ? p->kd_batch_stride : (long long)r.N * T * HD;
+  if (r.k0_bs < 0 || r.kd_blk < 0 || r.kd_bs < 0 || (r.k0_bs % 8) || (r.kd_blk % 8) || (r.kd_bs % 8))
+    return fail(E3_EINVAL, "strides must be non-negative multiples of 8 elements");
+  return E3_OK;
+}
+
+e3::Args make_args(const e3_problem* p, const Resolved& r) {
+  e3::Args a{};
+  a.cu = p->num_docs > 1 ? p->cu_seqlens_dev : nullptr;
+  a.ndocs = p->num_docs > 1 ? p->num_docs : 1;
+  a.B = p->B;
+  a.T = p->T;
+  a.Tkv = p->T_kv;
+  a.H = p->H;
+  a.N = r.N;
+  a.k0_bs = r.k0_bs;
+  a.kd_bs = r.kd_bs;
+  a.kd_blk = r.kd_blk;
+  a.scale = p->scale;
+  a.c2 = p->scale * 1.4426950408889634f;
+  a.layout = p->layout;
+  a.cp = p->cp;
+  a.rank = p->rank;
+  return a;
+}
+
+int check_ptrs(const char* const* names, const void* const* ptrs, int n) {
+  for (int i = 0; i < n; ++i) {
+    if (!ptrs[i]) return fail(E3_EINVAL, "%s is NULL", names[i]);
+    if (misaligned(ptrs[i])) return fail(E3_EINVAL, "%s is not 16-byte aligned", names[i]);
+  }
+  return E3_OK;
+}
+
+int fwd_impl(const e3_problem* p, const void* q, const void* k0, const void* v0, const void* kd,
+             const void* vd, void* out, float* lse, hipStream_t st, bool whole) {
+  Resolved r;
+  int rc = validate(p, r, whole);
+  if (rc) return rc;
+  if (p->T == 0) return ok();
+  {
+    const char* names[] = {"q", "k0", "v0", "out", "lse"};
+    const void* ptrs[] = {q, k0, v0, out, lse};
+    if ((rc = check_ptrs(names, ptrs, 5))) return rc;
+  }
+  if (r.N > 0) {
+    const char* names[] = {"kd", "vd"};
+    const void* ptrs[] = {kd, vd};
+    if ((rc = check_ptrs(names, ptrs, 2))) return rc;
+  }
+  e3::Args a = make_args(p, r);
+  a.q = q;
+  a.k0 = k0;
+  a.v0 = v0;
+  a.kd = kd;
+  a.vd = vd;
+  a.out = out;
+  a.lse = lse;
+  hipError_t e = e3::launch_fwd(a, p->dtype, p->D, st);
+  if (e != hipSuccess) return fail(E3_EHIP, "forward launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int bwd_impl(const e3_problem* p, const void* dout, const void* q, const void* k0, const void* v0,
+             const void* kd, const void* vd, const void* out, const float* lse, void* ws, void* dq,
+             void* dk0, void* dv0, void* dkd, void* dvd, hipStream_t st, bool whole) {
+  Resolved r;
+  int rc = validate(p, r, whole);
+  if (rc) return rc;
+  if (p->T == 0) return ok();
+  {
+    const char* names[] = {"dout", "q", "k0", "v0", "out", "lse", "workspace", "dq", "dk0", "dv0"};
+    const void* ptrs[] = {dout, q, k0, v0, out, lse, ws, dq, dk0, dv0};
+    if ((rc = check_ptrs(names, ptrs, 10))) return rc;
+  }
+  if (r.N > 0) {
+    const char* names[] = {"kd", "vd", "dkd", "dvd"};
+    const void* ptrs[] = {kd, vd, dkd, dvd};
+    if ((rc = check_ptrs(names, ptrs, 4))) return rc;
+  }
+  e3::Args a = make_args(p, r);
+  a.q = q;
+  a.k0 = k0;
+  a.v0 = v0;
+  a.kd = kd;
+  a.vd = vd;
+  a.dout = dout;
+  a.o_in = out;
+  a.lse_in = lse;
+  a.delta = static_cast<float*>(ws);
+  a.dq = dq;
+  a.dk0 = dk0;
+  a.dv0 = dv0;
+  a.dkd = dkd;
+  a.dvd = dvd;
+  hipError_t e = e3::launch_bwd(a, p->dtype, p->D, st);
+  if (e != hipSuccess) return fail(E3_EHIP, "backward launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+e3::Geo geo_of(const e3_problem* p) { return e3::Geo{p->layout, p->cp, p->rank, p->T, p->T_kv}; }
+
+int doc_lo_host(const e3_problem* p, int pos) {
+  return e3::doc_lo_of(p->cu_seqlens_host, p->num_docs > 1 ? p->num_docs : 1, pos);
+}
+
+}  // namespace
+
+extern "C" {
+
+int eagle3_abi_version(void) { return EAGLE3_ABI_VERSION; }
+
+const char* eagle3_last_error(void) { return g_err.c_str(); }
+
+size_t eagle3_bwd_workspace_bytes(const e3_problem* p) {
+  Resolved r;
+  if (validate(p, r, false, false)) return 0;
+  g_err.clear();
+  const size_t n = (size_t)p->B * p->H * p->T * sizeof(float);
+  return (n + 255) & ~(size_t)255;
+}
+
+int eagle3_attn_fwd(const e3_problem* p, const void* q, const void* k0, const void* v0, const void* kd,
+                    const void* vd, void* out, float* lse, hipStream_t stream) {
+  return fwd_impl(p, q, k0, v0, kd, vd, out, lse, stream, true);
+}
+
+int eagle3_shard_fwd(const e3_problem* p, const void* q, const void* k0, const void* v0,
+                     const void* kd, const void* vd, void* out, float* lse, hipStream_t stream) {
+  return fwd_impl(p, q, k0, v0, kd, vd, out, lse, stream, false);
+}
+
+int eagle3_attn_bwd(const e3_problem* p, const void* dout, const void* q, const void* k0,
+                    const void* v0, const void* kd, const void* vd, const void* out, const float* lse,
+                    void* workspace, void* dq, void* dk0, void* dv0, void* dkd, void* dvd,
+                    hipStream_t stream) {
+  return bwd_impl(p, dout, q, k0, v0, kd, vd, out, lse, workspace, dq, dk0, dv0, dkd, dvd, stream, true);
+}
+
+int eagle3_shard_bwd(const e3_problem* p, const void* dout, const void* q, const void* k0,
+                     const void* v0, const void* kd, const void* vd, const void* out, const float* lse,
+                     void* workspace, void* dq, void* dk0, void* dv0, void* dkd, void* dvd,
+                     hipStream_t stream) {
+  return bwd_impl(p, dout, q, k0, v0, kd, vd, out, lse, workspace, dq, dk0, dv0, dkd, dvd, stream, false);
+}
+
+int lse_merge(float* out, float* lse, const float* block_out, const float* block_lse, int B, int T,
+              int H, int D, int block_lse_layout, hipStream_t stream) {
+  if (B < 1 || T < 0 || H < 1 || D < 4 || D % 4 != 0)
+    return fail(E3_EINVAL, "lse_merge: bad shape B=%d T=%d H=%d D=%d (D must be a multiple of 4)", B, T, H, D);
+  if (block_lse_layout != 0 && block_lse_layout != 1)
+    return fail(E3_EINVAL, "lse_merge: block_lse_layout must be 0 ([B,H,T]) or 1 ([B,T,H])");
+  if (T == 0) return ok();
+  const char* names[] = {"out", "lse", "block_out", "block_lse"};
+  const void* ptrs[] = {out, lse, block_out, block_lse};
+  for (int i = 0; i < 4; ++i) {
+    if (!ptrs[i]) return fail(E3_EINVAL, "lse_merge: %s is NULL", names[i]);
+    if (reinterpret_cast<uintptr_t>(ptrs[i]) & 3u) return fail(E3_EINVAL, "lse_merge: %s misaligned", names[i]);
+  }
+  if ((reinterpret_cast<uintptr_t>(out) | reinterpret_cast<uintptr_t>(block_out)) & 15u)
+    return fail(E3_EINVAL, "lse_merge: out and block_out must be 16-byte aligned");
+  hipError_t e = e3::launch_lse_merge(out, lse, block_out, block_lse, B, T, H, D, block_lse_layout, stream);
+  if (e != hipSuccess) return fail(E3_EHIP, "lse_merge launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int eagle3_query_positions(const e3_problem* p, int64_t* pos) {
+  Resolved r;
+  int rc = validate(p, r, false, false);
+  if (rc) return rc;
+  if (!pos && p->T) return fail(E3_EINVAL, "pos_host is NULL");
+  const e3::Geo g = geo_of(p);
+  for (int ri = 0; ri < g.nruns(); ++ri) {
+    int ls, len, gb;
+    g.run(ri, ls, len, gb);
+    for (int i = 0; i < len; ++i) pos[ls + i] = gb + i;
+  }
+  return ok();
+}
+
+int64_t eagle3_pair_count(const e3_problem* p) {
+  Resolved r;
+  int rc = validate(p, r, false, false);
+  if (rc) return rc;
+  const e3::Geo g = geo_of(p);
+  int64_t n = 0;
+  for (int ri = 0; ri < g.nruns(); ++ri) {
+    int ls, len, gb;
+    g.run(ri, ls, len, gb);
+    for (int i = 0; i < len; ++i) n += (gb + i) - doc_lo_host(p, gb + i) + 1;
+  }
+  g_err.clear();
+  return n;
+}
+
+int eagle3_fwd_tiles(const e3_problem* p, int32_t* tile_rows) {
+  Resolved r;
+  int rc = validate(p, r, false, false);
+  if (rc) return rc;
+  if (tile_rows) *tile_rows = e3::fwd_tile_rows();
+  g_err.clear();
+  return geo_of(p).ntiles(e3::fwd_tile_rows());
+}
+
+int eagle3_fwd_tile_segments(const e3_problem* p, int tile, int32_t* rows, int32_t* seg, int max_segments) {
+  Resolved r;
+  int rc = validate(p, r, false, false);
+  if (rc) return rc;
+  const e3::Geo g = geo_of(p);
+  const int BM = e3::fwd_tile_rows(), BN = e3::fwd_tile_keys();
+  if (tile < 0 || tile >= g.ntiles(BM)) return fail(E3_EINVAL, "tile %d out of range", tile);
+  int row0, nrows, gpos0;
+  g.qtile(tile, BM, row0, nrows, gpos0);
+  if (rows) {
+    rows[0] = row0;
+    rows[1] = row0 + nrows;
+  }
+  const int g_min = gpos0, g_max = gpos0 + nrows - 1;
+  const int lo_min = doc_lo_host(p, g_min), lo_max = doc_lo_host(p, g_max);
+  e3::SegIter it;
+  it.begin(g, lo_min, g_max + 1, BN);
+  int n = 0;
+  while (it.valid) {
+    if (seg && n < max_segments) {
+      const int s0 = it.s0, e = (s0 + BN) < it.b ? (s0 + BN) : it.b;
+      const bool interior = s0 >= it.a && s0 + BN <= it.b && s0 >= lo_max && s0 + BN - 1 <= g_min;
+      seg[3 * n + 0] = s0;
+      seg[3 * n + 1] = e;
+      seg[3 * n + 2] = interior ? 0 : 1;
+    }
+    ++n;
+    it.next(g, BN);
+  }
+  g_err.clear();
+  return n;
+}
+
+}  // extern "C"

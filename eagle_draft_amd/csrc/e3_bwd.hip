@@ -1,0 +1,496 @@
+// EAGLE-3 mixed attention, backward (gfx950).
+//
+// The backward runs against the MERGED joint-softmax out/lse (ring_attention page,
+// `_CachedRingAttention`; ulysses_attention page, `_block0_backward`;
+// zigzag_ring_attention page, `zigzag_ring_flash_attn_varlen_backward`), so block-0
+// probabilities are P = exp(scale*q.k - lse) with the lse that includes the diagonal
+// blocks, and the diagonal gradients follow in closed form.
+//
+// Three kernels, no atomics (every output element has one writer):
+//   delta_kernel  delta[b,h,t] = <dO_t, O_t> (O = the stored merged out)
+//   dkdv_kernel   one workgroup per 128 block-0 keys (32 per wave, lane = key);
+//                 loops over the query tiles that see them:
+//                   S = Q K^T, P, dP = dO V^T, dS = P (dP - delta),
+//                   dV += P^T dO, dK += scale dS^T Q
+//                 Q and dO tiles are staged in LDS both as-is and transposed.
+//   dq_kernel     one workgroup per 128 query rows (lane = query, as in the
+//                 forward); loops over the visible key tiles in ring order:
+//                   dQ += dS K; then the epilogue adds the diagonal terms
+//                   pi = exp(y - lse), dpi = <dO, vd>, ds = pi (dpi - delta),
+//                   dq += scale ds kd, dkd = scale ds q, dvd = pi dO.
+#include "e3_common.h"
+
+namespace e3 {
+
+// ---------------------------------------------------------------------------
+// delta = rowsum(dO * O)
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(256) void delta_kernel(const Args a) {
+  constexpr int LPR = D / 8;
+  constexpr int RPB = 256 / LPR;   // rows (b, t, h) per block
+  const int lane = threadIdx.x;
+  const long long r = (long long)blockIdx.x * RPB + lane / LPR;   // row over B*T*H
+  const long long nrow = (long long)a.B * a.T * a.H;
+  const bool valid = r < nrow;
+  const long long rr = valid ? r : 0;
+  const int cc = (lane % LPR) * 8;
+  const f32x8 x = load8f(reinterpret_cast<const T*>(a.dout) + rr * D + cc);
+  const f32x8 y = load8f(reinterpret_cast<const T*>(a.o_in) + rr * D + cc);
+  float d = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) d += x[e] * y[e];
+  d = group_sum<LPR>(d);
+  if (valid && (lane % LPR) == 0) {
+    const long long h = rr % a.H, bt = rr / a.H, t = bt % a.T, b = bt / a.T;
+    a.delta[(b * a.H + h) * a.T + t] = d;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK0 / dV0
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+struct DkdvCfg {
+  static constexpr int BNK = 128;            // keys per workgroup (32 per wave)
+  static constexpr int BMQ = 64;             // query rows per iteration
+  static constexpr int PAD = 16 / (int)sizeof(T);
+  static constexpr int NSTR = D + PAD;       // natural Q / dO rows
+  static constexpr int TSTR = BMQ + PAD;     // transposed Q / dO rows
+  static constexpr int KS = D / 16;
+  static constexpr int DB = D / 32;
+  static constexpr int LDS = (2 * BMQ * NSTR + 2 * D * TSTR) * (int)sizeof(T) + 2 * BMQ * 4;
+};
+
+// Query tiles (rows of the share) that can see keys [k_lo, k_hi) with document
+// end doc_end(k_hi - 1): per run, rows whose global position lies in
+// [k_lo, dend). Tile starts are aligned to BMQ relative to the run start.
+struct QIter {
+  int run, ls, len, gb, t0, tend;
+  int qlo, qhi;
+  bool valid;
+  __device__ void seek(const Geo& g, int BMQ) {
+    while (run < g.nruns()) {
+      g.run(run, ls, len, gb);
+      const int lo = qlo > gb ? qlo : gb;
+      const int hi = qhi < gb + len ? qhi : gb + len;
+      if (lo < hi) {
+        t0 = ((lo - gb) / BMQ) * BMQ;   // offset within the run
+        tend = hi - gb;
+        valid = true;
+        return;
+      }
+      ++run;
+    }
+    valid = false;
+  }
+  __device__ void begin(const Geo& g, int qlo_, int qhi_, int BMQ) {
+    qlo = qlo_;
+    qhi = qhi_;
+    run = 0;
+    seek(g, BMQ);
+  }
+  __device__ void next(const Geo& g, int BMQ) {
+    t0 += BMQ;
+    if (t0 < tend) return;
+    ++run;
+    seek(g, BMQ);
+  }
+  __device__ int row0() const { return ls + t0; }
+  __device__ int nrows(int BMQ) const { return (len - t0) < BMQ ? (len - t0) : BMQ; }
+  __device__ int gpos0() const { return gb + t0; }
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(256, 1) void dkdv_kernel(const Args a) {
+  using C = DkdvCfg<T, D>;
+  using Op = typename V8<T>::type;
+  constexpr int BNK = C::BNK, BMQ = C::BMQ, KS = C::KS, DB = C::DB;
+  __shared__ __attribute__((aligned(16))) char smem[C::LDS];
+  T* Qs = reinterpret_cast<T*>(smem);
+  T* Os = Qs + BMQ * C::NSTR;
+  T* Qt = Os + BMQ * C::NSTR;
+  T* Ot = Qt + D * C::TSTR;
+  float* L2s = reinterpret_cast<float*>(Ot + D * C::TSTR);
+  float* Ds = L2s + BMQ;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
+  const int BH = a.B * a.H;
+  const int kt = blockIdx.x / BH, bh = blockIdx.x % BH, b = bh / a.H, h = bh % a.H;
+  const Geo geo{a.layout, a.cp, a.rank, a.T, a.Tkv};
+  const int kt0 = kt * BNK;
+  const int kt1 = (kt0 + BNK) < a.Tkv ? (kt0 + BNK) : a.Tkv;
+
+  const long long rs = (long long)a.H * D;
+  const T* k0b = reinterpret_cast<const T*>(a.k0) + (long long)b * a.k0_bs + (long long)h * D;
+  const T* v0b = reinterpret_cast<const T*>(a.v0) + (long long)b * a.k0_bs + (long long)h * D;
+  const T* qb = reinterpret_cast<const T*>(a.q) + (long long)b * a.T * rs + (long long)h * D;
+  const T* dob = reinterpret_cast<const T*>(a.dout) + (long long)b * a.T * rs + (long long)h * D;
+  const float* lseb = a.lse_in + ((long long)b * a.H + h) * a.T;
+  const float* delb = a.delta + ((long long)b * a.H + h) * a.T;
+
+  // This lane's key; a query at global position gm sees it iff s <= gm < s_hi.
+  const int s = kt0 + w * 32 + l32;
+  const bool svalid = s < a.Tkv;
+  const int s_hi = svalid ? doc_hi_of(a.cu, a.ndocs, s, a.Tkv) : 0;
+  Op kreg[KS], vreg[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    kreg[ks] = svalid ? load8(k0b + (long long)s * rs + 16 * ks + 8 * g) : zero8<T>();
+    vreg[ks] = svalid ? load8(v0b + (long long)s * rs + 16 * ks + 8 * g) : zero8<T>();
+  }
+  const int hi_min = doc_hi_of(a.cu, a.ndocs, kt0, a.Tkv);   // smallest document end of the tile
+  const int q_hi = doc_hi_of(a.cu, a.ndocs, kt1 - 1, a.Tkv);  // queries past this see no key
+
+  f32x16 dk[DB], dv[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      dk[db][j] = 0.f;
+      dv[db][j] = 0.f;
+    }
+  const float c2 = a.c2;
+
+  QIter it;
+  it.begin(geo, kt0, q_hi, BMQ);
+  TileLoad<T, BMQ, D, 256> qt, ot;
+  float lv = 0.f, dl = 0.f;
+  auto prefetch = [&]() {
+    const int r0 = it.row0(), nr = it.nrows(BMQ);
+    qt.load(qb + (long long)r0 * rs, rs, nr, tid);
+    ot.load(dob + (long long)r0 * rs, rs, nr, tid);
+    if (tid < BMQ) {
+      lv = tid < nr ? lseb[r0 + tid] * kLog2e : 0.f;
+      dl = tid < nr ? delb[r0 + tid] : 0.f;
+    }
+  };
+  if (it.valid) prefetch();
+  while (it.valid) {
+    const int nr = it.nrows(BMQ), gq0 = it.gpos0();
+    __syncthreads();
+    qt.store_nat(Qs, C::NSTR, tid);
+    qt.store_tr(Qt, C::TSTR, tid);
+    ot.store_nat(Os, C::NSTR, tid);
+    ot.store_tr(Ot, C::TSTR, tid);
+    if (tid < BMQ) {
+      L2s[tid] = lv;
+      Ds[tid] = dl;
+    }
+    __syncthreads();
+    it.next(geo, BMQ);
+    if (it.valid) prefetch();
+
+    // S = Q K^T and dP = dO V^T: two 32-query blocks, lane = key, 16 queries each.
+    f32x16 sp[2], dp[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        sp[mb][j] = 0.f;
+        dp[mb][j] = 0.f;
+      }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const Op qa = load8(Qs + (32 * mb + l32) * C::NSTR + 16 * ks + 8 * g);
+        mfma16(qa, kreg[ks], sp[mb]);
+        const Op oa = load8(Os + (32 * mb + l32) * C::NSTR + 16 * ks + 8 * g);
+        mfma16(oa, vreg[ks], dp[mb]);
+      }
+    }
+    const bool interior = nr == BMQ && kt0 + BNK <= a.Tkv && gq0 >= kt0 + BNK - 1 &&
+                          gq0 + BMQ - 1 < hi_min;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int m0 = 32 * mb + 8 * jj + 4 * g;
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(L2s + m0);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(Ds + m0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int j = 4 * jj + i;
+          float p = fast_exp2(sp[mb][j] * c2 - l4[i]);
+          if (!interior) {
+            const int m = m0 + i, gm = gq0 + m;
+            const bool vis = svalid && m < nr && gm >= s && gm < s_hi;
+            p = vis ? p : 0.f;
+          }
+          sp[mb][j] = p;
+          dp[mb][j] = p * (dp[mb][j] - d4[i]);
+        }
+      }
+    // dV^T += dO^T P, dK^T += Q^T dS over the 64 queries (4 k-steps of 16).
+#pragma unroll
+    for (int ks = 0; ks < BMQ / 16; ++ks) {
+      const Op pb = to_op(sp[ks >> 1], 8 * (ks & 1), T());
+      const Op sb = to_op(dp[ks >> 1], 8 * (ks & 1), T());
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const Op oa = load8(Ot + (32 * db + l32) * C::TSTR + 16 * ks + 8 * g);
+        mfma16(oa, pb, dv[db]);
+        const Op qa = load8(Qt + (32 * db + l32) * C::TSTR + 16 * ks + 8 * g);
+        mfma16(qa, sb, dk[db]);
+      }
+    }
+  }
+
+  // Write dK0 = scale * dK, dV0 (rows of keys no query sees are zeros).
+  if (svalid) {
+    T* dkb = reinterpret_cast<T*>(a.dk0) + (long long)b * a.k0_bs + (long long)h * D + (long long)s * rs;
+    T* dvb = reinterpret_cast<T*>(a.dv0) + (long long)b * a.k0_bs + (long long)h * D + (long long)s * rs;
+    typedef typename VecE<T, 4>::type v4;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        v4 x, y;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[i] = (T)(dk[db][4 * jj + i] * a.scale);
+          y[i] = (T)dv[db][4 * jj + i];
+        }
+        const int d0 = 32 * db + 8 * jj + 4 * g;
+        *reinterpret_cast<v4*>(dkb + d0) = x;
+        *reinterpret_cast<v4*>(dvb + d0) = y;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ (block 0) + closed-form diagonal gradients
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+struct DqCfg {
+  static constexpr int BM = 128;
+  static constexpr int BN = 64;
+  static constexpr int PAD = 16 / (int)sizeof(T);
+  static constexpr int NSTR = D + PAD;
+  static constexpr int TSTR = BN + PAD;
+  static constexpr int OSTR = D + 4;
+  static constexpr int KS = D / 16;
+  static constexpr int DB = D / 32;
+  static constexpr int LDS_KV = (2 * BN * NSTR + D * TSTR) * (int)sizeof(T);
+  static constexpr int LDS_EPI = 4 * 32 * OSTR * 4;
+  static constexpr int LDS = LDS_KV > LDS_EPI ? LDS_KV : LDS_EPI;
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(256, 2) void dq_kernel(const Args a) {
+  using C = DqCfg<T, D>;
+  using Op = typename V8<T>::type;
+  constexpr int BM = C::BM, BN = C::BN, KS = C::KS, DB = C::DB;
+  __shared__ __attribute__((aligned(16))) char smem[C::LDS];
+  T* Ks = reinterpret_cast<T*>(smem);
+  T* Vs = Ks + BN * C::NSTR;
+  T* Kt = Vs + BN * C::NSTR;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
+  const int BH = a.B * a.H;
+  const int trank = blockIdx.x / BH, bh = blockIdx.x % BH, b = bh / a.H, h = bh % a.H;
+  const Geo geo{a.layout, a.cp, a.rank, a.T, a.Tkv};
+  int row0, nrows, gpos0;
+  geo.qtile(trank, BM, row0, nrows, gpos0);
+
+  const long long rs = (long long)a.H * D;
+  const T* qb = reinterpret_cast<const T*>(a.q) + (long long)b * a.T * rs + (long long)h * D;
+  const T* dob = reinterpret_cast<const T*>(a.dout) + (long long)b * a.T * rs + (long long)h * D;
+  const T* k0b = reinterpret_cast<const T*>(a.k0) + (long long)b * a.k0_bs + (long long)h * D;
+  const T* v0b = reinterpret_cast<const T*>(a.v0) + (long long)b * a.k0_bs + (long long)h * D;
+  const float* lseb = a.lse_in + ((long long)b * a.H + h) * a.T;
+  const float* delb = a.delta + ((long long)b * a.H + h) * a.T;
+
+  const int qr = w * 32 + l32;
+  const bool qvalid = qr < nrows;
+  const int gq = gpos0 + qr;
+  const int loq = doc_lo_of(a.cu, a.ndocs, qvalid ? gq : gpos0);
+  const int g_min = gpos0, g_max = gpos0 + nrows - 1;
+  const int lo_min = doc_lo_of(a.cu, a.ndocs, g_min);
+  const int lo_max = doc_lo_of(a.cu, a.ndocs, g_max);
+  const float lq = qvalid ? lseb[row0 + qr] * kLog2e : 0.f;
+  const float dq_delta = qvalid ? delb[row0 + qr] : 0.f;
+
+  Op qreg[KS], oreg[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const long long off = (long long)(row0 + qr) * rs + 16 * ks + 8 * g;
+    qreg[ks] = qvalid ? load8(qb + off) : zero8<T>();
+    oreg[ks] = qvalid ? load8(dob + off) : zero8<T>();
+  }
+  f32x16 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[db][j] = 0.f;
+  const float c2 = a.c2;
+
+  SegIter it;
+  it.begin(geo, lo_min, g_max + 1, BN);
+  TileLoad<T, BN, D, 256> kt, vt;
+  if (it.valid) {
+    const int nv = a.Tkv - it.s0;
+    kt.load(k0b + (long long)it.s0 * rs, rs, nv, tid);
+    vt.load(v0b + (long long)it.s0 * rs, rs, nv, tid);
+  }
+  while (it.valid) {
+    const int s0 = it.s0, sa = it.a, sb = it.b;
+    __syncthreads();
+    kt.store_nat(Ks, C::NSTR, tid);
+    kt.store_tr(Kt, C::TSTR, tid);
+    vt.store_nat(Vs, C::NSTR, tid);
+    __syncthreads();
+    it.next(geo, BN);
+    if (it.valid) {
+      const int nv = a.Tkv - it.s0;
+      kt.load(k0b + (long long)it.s0 * rs, rs, nv, tid);
+      vt.load(v0b + (long long)it.s0 * rs, rs, nv, tid);
+    }
+
+    f32x16 st[2], dpt[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        st[kb][j] = 0.f;
+        dpt[kb][j] = 0.f;
+      }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const Op ka = load8(Ks + (32 * kb + l32) * C::NSTR + 16 * ks + 8 * g);
+        mfma16(ka, qreg[ks], st[kb]);
+        const Op va = load8(Vs + (32 * kb + l32) * C::NSTR + 16 * ks + 8 * g);
+        mfma16(va, oreg[ks], dpt[kb]);
+      }
+    }
+    const bool interior = s0 >= sa && s0 + BN <= sb && s0 >= lo_max && s0 + BN - 1 <= g_min;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        float p = fast_exp2(st[kb][j] * c2 - lq);
+        if (!interior) {
+          const int s = s0 + 32 * kb + 8 * (j >> 2) + 4 * g + (j & 3);
+          const bool vis = s >= sa && s < sb && s >= loq && s <= gq;
+          p = vis ? p : 0.f;
+        }
+        dpt[kb][j] = p * (dpt[kb][j] - dq_delta);
+      }
+#pragma unroll
+    for (int ks = 0; ks < BN / 16; ++ks) {
+      const Op sbv = to_op(dpt[ks >> 1], 8 * (ks & 1), T());
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const Op ka = load8(Kt + (32 * db + l32) * C::TSTR + 16 * ks + 8 * g);
+        mfma16(ka, sbv, acc[db]);
+      }
+    }
+  }
+
+  // ---- epilogue: stage dQ^T through LDS, then the diagonal terms row-major ----
+  __syncthreads();
+  float* Qw = reinterpret_cast<float*>(smem) + w * 32 * C::OSTR;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      f32x4 v;
+      v[0] = acc[db][4 * jj + 0];
+      v[1] = acc[db][4 * jj + 1];
+      v[2] = acc[db][4 * jj + 2];
+      v[3] = acc[db][4 * jj + 3];
+      *reinterpret_cast<f32x4*>(Qw + l32 * C::OSTR + 32 * db + 8 * jj + 4 * g) = v;
+    }
+  __syncthreads();
+
+  constexpr int LPR = D / 8;
+  constexpr int RPP = 64 / LPR;
+  const int lr = lane / LPR, cc = (lane % LPR) * 8;
+  const T* kdb = reinterpret_cast<const T*>(a.kd) + (long long)b * a.kd_bs + (long long)h * D + cc;
+  const T* vdb = reinterpret_cast<const T*>(a.vd) + (long long)b * a.kd_bs + (long long)h * D + cc;
+  T* dkdb = reinterpret_cast<T*>(a.dkd) + (long long)b * a.kd_bs + (long long)h * D + cc;
+  T* dvdb = reinterpret_cast<T*>(a.dvd) + (long long)b * a.kd_bs + (long long)h * D + cc;
+  T* dqb = reinterpret_cast<T*>(a.dq) + (long long)b * a.T * rs + (long long)h * D + cc;
+  const float scale = a.scale;
+  for (int pass = 0; pass < 32 / RPP; ++pass) {
+    const int rr = pass * RPP + lr;
+    const int tr = w * 32 + rr;
+    if (tr >= nrows) continue;
+    const long long row = row0 + tr;
+    f32x8 dqv = *reinterpret_cast<const f32x8*>(Qw + rr * C::OSTR + cc);
+    const f32x8 qv = load8f(qb + row * rs + cc);
+    const f32x8 ov = load8f(dob + row * rs + cc);
+    const float l2 = lseb[row] * kLog2e;
+    const float dl = delb[row];
+    for (int i0 = 0; i0 < a.N; i0 += 4) {
+      const int n = (a.N - i0) < 4 ? (a.N - i0) : 4;
+      f32x8 kv[4], vv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (i < n) {
+          const long long off = (long long)(i0 + i) * a.kd_blk + row * rs;
+          kv[i] = load8f(kdb + off);
+          vv[i] = load8f(vdb + off);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (i < n) {
+          float y = 0.f, dpi = 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            y += qv[e] * kv[i][e];
+            dpi += ov[e] * vv[i][e];
+          }
+          y = group_sum<LPR>(y);
+          dpi = group_sum<LPR>(dpi);
+          const float pi = fast_exp2(y * c2 - l2);
+          const float ds = pi * (dpi - dl);
+          f32x8 gk, gv;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            dqv[e] += ds * kv[i][e];
+            gk[e] = scale * ds * qv[e];
+            gv[e] = pi * ov[e];
+          }
+          const long long off = (long long)(i0 + i) * a.kd_blk + row * rs;
+          store8f(dkdb + off, gk);
+          store8f(dvdb + off, gv);
+        }
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dqv[e] *= scale;
+    store8f(dqb + row * rs, dqv);
+  }
+}
+
+template <typename T, int D>
+static hipError_t launch_bwd_t(const Args& a, hipStream_t st) {
+  const long long nrow = (long long)a.B * a.T * a.H;
+  if (nrow > 0) {
+    const long long nb = (nrow + (256 / (D / 8)) - 1) / (256 / (D / 8));
+    hipLaunchKernelGGL((delta_kernel<T, D>), dim3((unsigned)nb), dim3(256), 0, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const long long nk = (long long)((a.Tkv + DkdvCfg<T, D>::BNK - 1) / DkdvCfg<T, D>::BNK) * a.B * a.H;
+  if (nk > 0) {
+    hipLaunchKernelGGL((dkdv_kernel<T, D>), dim3((unsigned)nk), dim3(256), 0, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const Geo geo{a.layout, a.cp, a.rank, a.T, a.Tkv};
+  const long long nq = (long long)geo.ntiles(DqCfg<T, D>::BM) * a.B * a.H;
+  if (nq > 0) {
+    hipLaunchKernelGGL((dq_kernel<T, D>), dim3((unsigned)nq), dim3(256), 0, st, a);
+    return hipGetLastError();
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_bwd(const Args& a, int dtype, int D, hipStream_t st) {
+  if (dtype == 0) return D == 128 ? launch_bwd_t<bf16, 128>(a, st) : launch_bwd_t<bf16, 64>(a, st);
+  return D == 128 ? launch_bwd_t<float, 128>(a, st) : launch_bwd_t<float, 64>(a, st);
+}
+
+}  // namespace e3

@@ -1,0 +1,343 @@
+// Shared definitions of the EAGLE-3 mixed-attention HIP kernels (gfx950):
+// vector types, MFMA steps, DPP row reductions, and the share geometry (query
+// rows -> global positions, block-0 K/V segments in ring order) used by both the
+// kernels and the host driver.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace e3 {
+
+typedef __bf16 bf16;
+typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+enum { LAYOUT_FULL = 0, LAYOUT_CONTIGUOUS = 1, LAYOUT_ZIGZAG = 2, LAYOUT_HEADSHARD = 3 };
+
+// Kernel arguments (passed by value). Strides are in elements.
+struct Args {
+  const void* q;
+  const void* k0;
+  const void* v0;
+  const void* kd;
+  const void* vd;
+  const void* dout;
+  const void* o_in;     // merged out (backward input)
+  const float* lse_in;  // merged lse (backward input)
+  void* out;
+  float* lse;
+  float* delta;         // rowsum(dO * O), [B, H, T]
+  void* dq;
+  void* dk0;
+  void* dv0;
+  void* dkd;
+  void* dvd;
+  const int32_t* cu;    // device cu_seqlens (global document boundaries)
+  int ndocs;            // <= 1: one document
+  int B, T, Tkv, H, N;
+  long long k0_bs, kd_bs, kd_blk;
+  float scale;
+  float c2;             // scale * log2(e): scores are kept in the base-2 domain
+  int layout, cp, rank;
+};
+
+// ---------------------------------------------------------------------------
+// Share geometry (host and device)
+// ---------------------------------------------------------------------------
+
+// Query rows of a share come in runs of contiguous global positions:
+//   full / head shard: one run, positions 0..T-1
+//   contiguous rank r: one run, positions r*T .. r*T+T-1
+//   zig-zag rank r: run 0 = chunk r (early), run 1 = chunk 2cp-1-r (late), c = T/2 each
+// Block-0 K/V segments are visited in ring order: ring step j holds rank
+// (r - j) mod cp's K/V, i.e. chunk src (contiguous) or chunks {src, 2cp-1-src}
+// (zig-zag).
+struct Geo {
+  int layout, cp, rank, T, Tkv;
+
+  __host__ __device__ int nruns() const { return layout == LAYOUT_ZIGZAG ? 2 : 1; }
+
+  __host__ __device__ void run(int i, int& lstart, int& len, int& gbase) const {
+    if (layout == LAYOUT_ZIGZAG) {
+      const int c = T / 2;
+      lstart = i * c;
+      len = c;
+      gbase = (i == 0 ? rank : 2 * cp - 1 - rank) * c;
+    } else {
+      lstart = 0;
+      len = T;
+      gbase = (layout == LAYOUT_CONTIGUOUS) ? rank * T : 0;
+    }
+  }
+
+  __host__ __device__ int nsteps() const {
+    return (layout == LAYOUT_CONTIGUOUS || layout == LAYOUT_ZIGZAG) ? cp : 1;
+  }
+  __host__ __device__ int nparts() const { return layout == LAYOUT_ZIGZAG ? 2 : 1; }
+
+  __host__ __device__ void seg(int step, int part, int& a, int& b) const {
+    if (layout == LAYOUT_CONTIGUOUS) {
+      const int src = ((rank - step) % cp + cp) % cp;
+      a = src * T;
+      b = a + T;
+    } else if (layout == LAYOUT_ZIGZAG) {
+      const int c = T / 2;
+      const int src = ((rank - step) % cp + cp) % cp;
+      const int id = part == 0 ? src : 2 * cp - 1 - src;
+      a = id * c;
+      b = a + c;
+    } else {
+      a = 0;
+      b = Tkv;
+    }
+  }
+
+  // Number of query tiles of height BM over all runs.
+  __host__ __device__ int ntiles(int BM) const {
+    int n = 0;
+    for (int r = 0; r < nruns(); ++r) {
+      int ls, len, gb;
+      run(r, ls, len, gb);
+      n += (len + BM - 1) / BM;
+    }
+    return n;
+  }
+
+  // Query tile in launch order: the latest global positions (the most block-0
+  // keys) first. Returns the local first row, the row count and the global
+  // position of the first row.
+  __host__ __device__ void qtile(int trank, int BM, int& row0, int& nrows, int& gpos0) const {
+    for (int r = nruns() - 1; r >= 0; --r) {
+      int ls, len, gb;
+      run(r, ls, len, gb);
+      const int nt = (len + BM - 1) / BM;
+      if (trank < nt) {
+        const int t = nt - 1 - trank;
+        row0 = ls + t * BM;
+        nrows = (len - t * BM) < BM ? (len - t * BM) : BM;
+        gpos0 = gb + t * BM;
+        return;
+      }
+      trank -= nt;
+    }
+    row0 = 0;
+    nrows = 0;
+    gpos0 = 0;
+  }
+};
+
+// Walks the block-0 key tiles of width BN that a query tile can see: segment by
+// segment in ring order, each segment clipped to the key window [wlo, whi).
+// Tile starts are aligned to BN relative to the segment start; keys of a tile
+// outside [a, b) or outside a row's visible range are masked by the kernel.
+struct SegIter {
+  int step, part, a, b, s0, end, wlo, whi;
+  bool valid;
+
+  __host__ __device__ void seek(const Geo& g, int BN) {
+    while (true) {
+      if (step >= g.nsteps()) {
+        valid = false;
+        return;
+      }
+      g.seg(step, part, a, b);
+      const int lo = a > wlo ? a : wlo;
+      const int hi = b < whi ? b : whi;
+      if (lo < hi) {
+        s0 = a + ((lo - a) / BN) * BN;
+        end = hi;
+        valid = true;
+        return;
+      }
+      if (++part >= g.nparts()) {
+        part = 0;
+        ++step;
+      }
+    }
+  }
+  __host__ __device__ void begin(const Geo& g, int wlo_, int whi_, int BN) {
+    wlo = wlo_;
+    whi = whi_;
+    step = 0;
+    part = 0;
+    seek(g, BN);
+  }
+  __host__ __device__ void next(const Geo& g, int BN) {
+    s0 += BN;
+    if (s0 < end) return;
+    if (++part >= g.nparts()) {
+      part = 0;
+      ++step;
+    }
+    seek(g, BN);
+  }
+};
+
+// Document bounds from cu_seqlens (non-decreasing, cu[0] = 0, cu[nd] = S).
+__host__ __device__ inline int doc_lo_of(const int32_t* cu, int nd, int pos) {
+  if (nd <= 1) return 0;
+  int lo = 0, hi = nd;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (cu[mid] <= pos) lo = mid; else hi = mid;
+  }
+  return cu[lo];
+}
+__host__ __device__ inline int doc_hi_of(const int32_t* cu, int nd, int pos, int S) {
+  if (nd <= 1) return S;
+  int lo = 0, hi = nd;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (cu[mid] <= pos) lo = mid; else hi = mid;
+  }
+  return cu[hi];
+}
+
+// ---------------------------------------------------------------------------
+// Device helpers
+// ---------------------------------------------------------------------------
+template <typename T> struct V8;
+template <> struct V8<bf16> { typedef bf16x8 type; };
+template <> struct V8<float> { typedef f32x8 type; };
+
+// One k = 16 slice of a 32x32 output block. bf16: one v_mfma_f32_32x32x16_bf16.
+// f32: eight v_mfma_f32_32x32x2_f32 over the same per-lane data (lane group g
+// holds k = 8g + i in its i-th element; step i pairs element i of both groups).
+__device__ __forceinline__ void mfma16(const bf16x8& a, const bf16x8& b, f32x16& c) {
+  c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ void mfma16(const f32x8& a, const f32x8& b, f32x16& c) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[i], c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+#define E3_DPP(x, ctrl) \
+  __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, (x)), (ctrl), 0xF, 0xF, true))
+
+// Sum over aligned groups of `W` lanes (W = 8 or 16); every lane gets the sum.
+template <int W>
+__device__ __forceinline__ float group_sum(float x) {
+  x += E3_DPP(x, 0xB1);   // quad_perm [1,0,3,2]
+  x += E3_DPP(x, 0x4E);   // quad_perm [2,3,0,1]
+  x += E3_DPP(x, 0x141);  // row_half_mirror: the other quad of 8
+  if constexpr (W == 16) x += E3_DPP(x, 0x140);  // row_mirror: the other half of 16
+  return x;
+}
+
+__device__ __forceinline__ float xor32(float x) {
+  return __shfl_xor(x, 32);
+}
+
+// Convert 8 accumulator values (fp32) to an MFMA operand of element type T.
+__device__ __forceinline__ bf16x8 to_op(const f32x16& v, int off, bf16) {
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (bf16)v[off + i];
+  return r;
+}
+__device__ __forceinline__ f32x8 to_op(const f32x16& v, int off, float) {
+  f32x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = v[off + i];
+  return r;
+}
+
+template <typename T>
+__device__ __forceinline__ typename V8<T>::type load8(const T* p) {
+  return *reinterpret_cast<const typename V8<T>::type*>(p);
+}
+template <typename T>
+__device__ __forceinline__ typename V8<T>::type zero8() {
+  typename V8<T>::type r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (T)0.f;
+  return r;
+}
+template <typename T>
+__device__ __forceinline__ f32x8 load8f(const T* p) {
+  const typename V8<T>::type v = load8(p);
+  f32x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (float)v[i];
+  return r;
+}
+template <typename T>
+__device__ __forceinline__ void store8f(T* p, const f32x8& v) {
+  typename V8<T>::type r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (T)v[i];
+  *reinterpret_cast<typename V8<T>::type*>(p) = r;
+}
+
+// ---------------------------------------------------------------------------
+// Global -> LDS tile staging. A tile is R rows x D columns of T; thread t holds
+// 4 consecutive rows x E columns. The natural copy keeps [row][col]; the
+// transposed copy is [col][row] with the rows of each 16-row group stored in
+// the order {0-3, 8-11, 4-7, 12-15}, so that an MFMA operand read of 8
+// consecutive elements at offset 8g of a group yields rows {4g..4g+3,
+// 8+4g..8+4g+3}: the row order in which a 32x32 accumulator holds its rows.
+// ---------------------------------------------------------------------------
+template <typename T, int E>
+struct VecE {
+  typedef T type __attribute__((ext_vector_type(E)));
+};
+
+template <typename T, int R, int D, int NT>
+struct TileLoad {
+  static constexpr int E = R * D / (NT * 4);
+  static_assert(E >= 1 && (E & (E - 1)) == 0, "tile does not split evenly");
+  static constexpr int CPR = D / E;       // column chunks per row
+  typedef typename VecE<T, E>::type vec;
+  typedef typename VecE<T, 4>::type vec4;
+  vec r[4];
+
+  // rows [row0, row0+R) of a [rows, H*D] tensor (row stride rs); rows at or past
+  // `rows_valid` (relative to row0) read as zero.
+  __device__ __forceinline__ void load(const T* base, long long rs, int rows_valid, int tid) {
+    const int cc = tid % CPR, rg = tid / CPR;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rr = rg * 4 + i;
+      if (rr < rows_valid) {
+        r[i] = *reinterpret_cast<const vec*>(base + (long long)rr * rs + cc * E);
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) r[i][e] = (T)0.f;
+      }
+    }
+  }
+  __device__ __forceinline__ void store_nat(T* lds, int stride, int tid) const {
+    const int cc = tid % CPR, rg = tid / CPR;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<vec*>(lds + (rg * 4 + i) * stride + cc * E) = r[i];
+  }
+  __device__ __forceinline__ void store_tr(T* lds, int stride, int tid) const {
+    const int cc = tid % CPR, rg = tid / CPR;
+    const int a = rg & 3;
+    const int slot = ((a & 1) << 1) | (a >> 1);
+    const int col = (rg >> 2) * 16 + slot * 4;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      vec4 v;
+      v[0] = r[0][e];
+      v[1] = r[1][e];
+      v[2] = r[2][e];
+      v[3] = r[3][e];
+      *reinterpret_cast<vec4*>(lds + (cc * E + e) * stride + col) = v;
+    }
+  }
+};
+
+}  // namespace e3

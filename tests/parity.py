@@ -1,0 +1,93 @@
+"""Helpers of the GPU parity tests: run the HIP path (through the C ABI) and the
+CPU oracle on the same seeded inputs and compare them."""
+from __future__ import annotations
+
+import sys
+import time
+
+import numpy as np
+import torch
+
+import eagle_draft_amd as e3
+import oracle
+import synth
+
+# Tolerances: bf16 -- out max-abs 2e-2, lse max-abs 1e-2, dq/dk/dv relative
+# Frobenius 3e-2 (dk and dv over all blocks together); fp32 -- 1e-5 on all.
+TOL = {"bf16": dict(out=2e-2, lse=1e-2, grad=3e-2), "f32": dict(out=1e-5, lse=1e-5, grad=1e-5)}
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def problem(w: synth.Workload, device="cuda") -> e3.Problem:
+    return e3.Problem(w.B, w.T, w.T_kv, w.H, w.D, w.num_blocks, w.scale, dtype=w.torch_dtype,
+                      layout=w.layout, cp=w.cp, rank=w.rank, cu_seqlens=w.cu_seqlens(),
+                      device=device)
+
+
+def run_hip(w: synth.Workload, inp: dict, device="cuda"):
+    prob = problem(w, device)
+    d = {k: v.to(device) for k, v in inp.items()}
+    out, lse = e3.fwd(prob, d["q"], d["k0"], d["v0"], d["kd"], d["vd"])
+    grads = e3.bwd(prob, d["dout"], d["q"], d["k0"], d["v0"], d["kd"], d["vd"], out, lse)
+    torch.cuda.synchronize()
+    return out.cpu(), lse.cpu(), [g.cpu() for g in grads]
+
+
+def oracle_cp(w):
+    return w.cp if w.layout in ("contiguous", "zigzag") else 1
+
+
+def run_oracle(w: synth.Workload, inp: dict, heads=None, rows=256):
+    f = {k: v.double().numpy() for k, v in inp.items()}
+    cu = w.cu_seqlens()
+    out, lse = oracle.forward(f["q"], f["k0"], f["v0"], f["kd"], f["vd"], w.scale, cu, w.layout,
+                              oracle_cp(w), w.rank, heads=heads, rows=rows)
+    grads = oracle.backward(f["dout"], f["q"], f["k0"], f["v0"], f["kd"], f["vd"], w.scale, cu,
+                            w.layout, oracle_cp(w), w.rank, out=out, lse=lse, heads=heads, rows=rows)
+    return out, lse, grads
+
+
+def rel(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    nb = np.linalg.norm(b)
+    return float(np.linalg.norm(a - b) / nb) if nb > 0 else float(np.linalg.norm(a))
+
+
+def compare(w, hip, ref, heads=None):
+    """Returns the error metrics of the HIP result against the oracle."""
+    out, lse, (dq, dk0, dv0, dkd, dvd) = hip
+    rout, rlse, (rdq, rdk0, rdv0, rdkd, rdvd) = ref
+    if heads is not None:
+        hs = list(heads)
+        out, dq, dk0, dv0 = out[:, :, hs], dq[:, :, hs], dk0[:, :, hs], dv0[:, :, hs]
+        dkd, dvd = dkd[:, :, :, hs], dvd[:, :, :, hs]
+        lse = lse[:, hs]
+    f = lambda t: t.double().numpy()
+    m = {
+        "out": float(np.abs(f(out) - rout).max()) if rout.size else 0.0,
+        "lse": float(np.abs(f(lse) - rlse).max()) if rlse.size else 0.0,
+        "dq": rel(f(dq), rdq),
+        "dk": rel(np.concatenate([f(dk0).ravel(), f(dkd).ravel()]),
+                  np.concatenate([rdk0.ravel(), rdkd.ravel()])),
+        "dv": rel(np.concatenate([f(dv0).ravel(), f(dvd).ravel()]),
+                  np.concatenate([rdv0.ravel(), rdvd.ravel()])),
+    }
+    if w.N > 0:
+        m["dk0"] = rel(f(dk0), rdk0)
+        m["dkd"] = rel(f(dkd), rdkd)
+    for k, v in m.items():
+        assert np.isfinite(v), (k, v)
+    return m
+
+
+def assert_within(w, m):
+    t = TOL[w.dtype]
+    assert m["out"] <= t["out"], m
+    assert m["lse"] <= t["lse"], m
+    for k in ("dq", "dk", "dv"):
+        assert m[k] <= t["grad"], m

@@ -1,0 +1,194 @@
+"""CPU tests of the C-ABI library: it loads, exports every declared symbol,
+rejects bad arguments before launching anything, and its shard driver (query
+positions, pair counts, ring-ordered key tiles) agrees with the oracle. No GPU
+is touched: only host-side entry points and validation failures are called."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+import eagle_draft_amd as e3
+import oracle
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "eagle3_attn.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*[A-Za-z_][\w\s\*]*?\b([a-z_0-9]+)\s*\(", text, flags=re.M)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = e3.lib()
+    names = declared_functions()
+    assert "eagle3_attn_fwd" in names and "lse_merge" in names and "eagle3_shard_bwd" in names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.eagle3_abi_version() == e3.ABI_VERSION
+
+
+def prob(**kw):
+    d = dict(B=1, T=256, T_kv=256, H=2, D=128, num_blocks=3, scale=0.088, dtype=torch.bfloat16)
+    d.update(kw)
+    return e3.Problem(**d)
+
+
+BAD = [
+    (dict(D=96), e3.E3_EUNSUPPORTED, "head dim"),
+    (dict(num_blocks=0), e3.E3_EINVAL, "num_blocks"),
+    (dict(num_blocks=17), e3.E3_EINVAL, "num_blocks"),
+    (dict(scale=float("nan")), e3.E3_EINVAL, "scale"),
+    (dict(scale=-1.0), e3.E3_EINVAL, "scale"),
+    (dict(T_kv=128), e3.E3_EINVAL, "T_kv"),
+    (dict(layout="headshard", cp=3, T=256, T_kv=256), e3.E3_EINVAL, "Ulysses"),
+    (dict(layout="zigzag", cp=2, T=255, T_kv=510), e3.E3_EINVAL, "even"),
+    (dict(layout="zigzag", cp=2, B=2, T=256, T_kv=512), e3.E3_EINVAL, "B must be 1"),
+    (dict(layout="contiguous", cp=2, rank=2, T=256, T_kv=512), e3.E3_EINVAL, "rank"),
+    (dict(layout="contiguous", cp=2, rank=0, T=256, T_kv=256), e3.E3_EINVAL, "cp*T"),
+    (dict(cu_seqlens=[0, 100, 200]), e3.E3_EINVAL, "ends at"),
+    (dict(cu_seqlens=[1, 100, 256]), e3.E3_EINVAL, "must be 0"),
+    (dict(cu_seqlens=[0, 200, 100, 256]), e3.E3_EINVAL, "non-decreasing"),
+    (dict(cu_seqlens=[0, 100, 256], B=2), e3.E3_EINVAL, "B == 1"),
+    (dict(layout="zigzag", cp=2, T=256, T_kv=512, cu_seqlens=[0, 100, 512]), e3.E3_EUNSUPPORTED, "ZIGZAG"),
+]
+
+
+@pytest.mark.parametrize("kw,code,msg", BAD)
+def test_invalid_problems_are_rejected_before_launch(kw, code, msg):
+    p = prob(**kw)
+    lib = e3.lib()
+    fake = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+    rc = lib.eagle3_shard_fwd(p.ref(), fake, fake, fake, fake, fake, fake, fake, None)
+    assert rc == code
+    assert msg in lib.eagle3_last_error().decode()
+    rc = lib.eagle3_shard_bwd(p.ref(), *([fake] * 14), None)
+    assert rc == code
+    assert lib.eagle3_bwd_workspace_bytes(p.ref()) == 0
+
+
+def test_null_and_misaligned_pointers_are_rejected():
+    lib = e3.lib()
+    p = prob()
+    a = ctypes.c_void_p(0x1000)
+    rc = lib.eagle3_attn_fwd(p.ref(), None, a, a, a, a, a, a, None)
+    assert rc == e3.E3_EINVAL and "q is NULL" in lib.eagle3_last_error().decode()
+    rc = lib.eagle3_attn_fwd(p.ref(), a, a, a, ctypes.c_void_p(0x1008), a, a, a, None)
+    assert rc == e3.E3_EINVAL and "kd is not 16-byte aligned" in lib.eagle3_last_error().decode()
+    rc = lib.eagle3_attn_bwd(p.ref(), *([a] * 13), None, None)
+    assert rc == e3.E3_EINVAL and "dvd is NULL" in lib.eagle3_last_error().decode()
+    # the full-sequence entry points refuse a ring share
+    q = prob(layout="zigzag", cp=2, T=256, T_kv=512)
+    rc = lib.eagle3_attn_fwd(q.ref(), *([a] * 7), None)
+    assert rc == e3.E3_EINVAL and "eagle3_shard_fwd" in lib.eagle3_last_error().decode()
+    # lse_merge shape checks
+    rc = lib.lse_merge(a, a, a, a, 1, 4, 2, 6, 0, None)
+    assert rc == e3.E3_EINVAL
+    rc = lib.lse_merge(a, a, a, a, 1, 4, 2, 8, 2, None)
+    assert rc == e3.E3_EINVAL
+    # an empty problem is a valid no-op
+    z = prob(T=0, T_kv=0)
+    assert lib.eagle3_attn_fwd(z.ref(), *([None] * 7), None) == e3.E3_OK
+    assert lib.eagle3_attn_bwd(z.ref(), *([None] * 14), None) == e3.E3_OK
+    assert lib.lse_merge(None, None, None, None, 1, 0, 2, 8, 0, None) == e3.E3_OK
+
+
+def test_workspace_bytes():
+    p = prob(B=1, T=1000, T_kv=1000, H=3)
+    assert p.workspace_bytes() == ((1 * 3 * 1000 * 4 + 255) // 256) * 256
+
+
+SHARES = [
+    ("full", 1000, 1, 0, None),
+    ("full", 700, 1, 0, [0, 5, 300, 300, 700]),    # includes an empty document
+    ("headshard", 1024, 4, 2, [0, 256, 1000, 1024]),
+    ("contiguous", 320, 4, 0, None),
+    ("contiguous", 320, 4, 3, None),
+    ("contiguous", 300, 3, 1, [0, 100, 450, 900]),
+    ("zigzag", 256, 4, 1, None),
+    ("zigzag", 300, 3, 2, None),     # chunk 150: ragged tiles
+    ("zigzag", 16384, 8, 3, None),   # the zig-zag workload's geometry
+]
+
+
+def share_problem(layout, T, cp, rank, cu):
+    Tkv = T * cp if layout in ("contiguous", "zigzag") else T
+    return e3.Problem(1, T, Tkv, 2, 128, 3, 0.1, layout=layout, cp=cp if layout != "full" else 1,
+                      rank=rank, cu_seqlens=cu)
+
+
+@pytest.mark.parametrize("layout,T,cp,rank,cu", SHARES)
+def test_shard_driver_positions_and_pair_counts(layout, T, cp, rank, cu):
+    p = share_problem(layout, T, cp, rank, cu)
+    pos = p.query_positions()
+    ocp = cp if layout in ("contiguous", "zigzag") else 1
+    np.testing.assert_array_equal(pos, oracle.query_positions(layout, T, ocp, rank))
+    assert p.pair_count() == oracle.pair_count(layout, T, ocp, rank, cu)
+
+
+@pytest.mark.parametrize("layout,T,cp,rank,cu", SHARES)
+def test_shard_driver_key_tiles_cover_exactly_the_visible_keys(layout, T, cp, rank, cu):
+    """Every query row counts each visible block-0 key exactly once over the
+    key tiles the kernel visits; unmasked tiles are fully visible to every row
+    of their query tile; the tiles of a segment follow the ring order."""
+    p = share_problem(layout, T, cp, rank, cu)
+    ocp = cp if layout in ("contiguous", "zigzag") else 1
+    qpos = oracle.query_positions(layout, T, ocp, rank)
+    lo = oracle.doc_start(cu, qpos)
+    ntiles, BM = p.fwd_tiles()
+    covered = np.zeros(T, dtype=bool)
+    heavy = []
+    if T > 4096:
+        tiles = list(range(0, ntiles, max(1, ntiles // 16)))
+    else:
+        tiles = range(ntiles)
+    for t in tiles:
+        (r0, r1), segs = p.fwd_tile_segments(t)
+        assert 0 < r1 - r0 <= BM
+        covered[r0:r1] = True
+        rows = np.arange(r0, r1)
+        g, l = qpos[rows], lo[rows]
+        assert np.all(np.diff(g) == 1)               # a tile is one run of positions
+        counts = np.zeros((len(rows), ), dtype=np.int64)
+        for (s0, s1, masked) in segs:
+            ks = np.arange(s0, s1)
+            vis = (ks[None, :] >= l[:, None]) & (ks[None, :] <= g[:, None])
+            counts += vis.sum(axis=1)
+            if not masked:
+                assert vis.all()
+        np.testing.assert_array_equal(counts, g - l + 1)
+        # no key counted twice: the tiles' clipped ranges are disjoint
+        spans = sorted((s0, s1) for (s0, s1, _) in segs)
+        for (a0, a1), (b0, b1) in zip(spans, spans[1:]):
+            assert a1 <= b0
+        heavy.append(int(g[0]))
+        if layout in ("contiguous", "zigzag"):
+            # the visited K/V chunks follow the ring: step j holds rank (r - j) mod cp
+            c = T if layout == "contiguous" else T // 2
+            order = []
+            for (s0, _, _) in segs:
+                ch = s0 // c
+                src = ch if ch < ocp else 2 * ocp - 1 - ch
+                if not order or order[-1] != src:
+                    order.append(src)
+            ring = [s for s, _ in oracle.ring_steps(layout, ocp, rank)]
+            assert order == [s for s in ring if s in order]
+    if T <= 4096:
+        assert covered.all()
+    if cu is None and layout != "zigzag":
+        assert heavy == sorted(heavy, reverse=True)    # latest positions (most keys) launch first
+
+
+def test_workload_pair_counts_match_golden():
+    import json
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "pair_counts.json")))
+    for name in synth.WORKLOADS:
+        w = synth.workload(name)
+        dt = torch.float32 if w.dtype == "f32" else torch.bfloat16
+        p = e3.Problem(w.B, w.T, w.T_kv, w.H, w.D, w.num_blocks, w.scale, dtype=dt,
+                       layout=w.layout, cp=w.cp, rank=w.rank, cu_seqlens=w.cu_seqlens())
+        assert p.pair_count() == g[name]["P0"], name

@@ -1,0 +1,125 @@
+"""GPU parity at sizes the oracle finishes in seconds: the HIP path (through the
+C ABI) against the CPU oracle, element by element, on the same seeded inputs.
+Cases span several tiles, ragged tails, several documents (one empty), one-row
+documents, num_blocks = 1, B > 1, both head dims and every layout."""
+import numpy as np
+import pytest
+import torch
+
+import eagle_draft_amd as e3
+import oracle
+import synth
+from tests.parity import assert_within, compare, run_hip, run_oracle, say
+
+pytestmark = pytest.mark.gpu
+
+W = synth.small_workload
+CASES = {
+    "bf16_full_384": W(S=384, H=2, D=128, num_blocks=3),
+    "bf16_full_ragged_1000": W(S=1000, H=3, D=128, num_blocks=4),
+    "bf16_full_d64": W(S=520, H=2, D=64, num_blocks=3),
+    "bf16_nb1": W(S=400, H=2, D=128, num_blocks=1),
+    "bf16_batch2": W(B=2, S=300, H=2, D=128, num_blocks=2),
+    "bf16_varlen": W(S=1200, H=2, D=128, num_blocks=3, doc_lens=[1, 300, 0, 77, 500, 1, 321]),
+    "bf16_varlen_nb8": W(S=2048, H=2, D=128, num_blocks=8, doc_lens=[700, 900, 448]),
+    "bf16_scaled_half": W(S=640, H=2, D=128, num_blocks=8, gen_scale=0.5),
+    "f32_tiny_like": W(dtype="f32", S=256, H=2, D=64, num_blocks=3),
+    "f32_ragged": W(dtype="f32", S=333, H=2, D=64, num_blocks=2),
+    "f32_d128": W(dtype="f32", S=200, H=1, D=128, num_blocks=3),
+    "contig_r0": W(S=1024, H=2, D=128, num_blocks=3, layout="contiguous", cp=4, rank=0, chunk=256),
+    "contig_r3": W(S=1024, H=2, D=128, num_blocks=3, layout="contiguous", cp=4, rank=3, chunk=256),
+    "contig_varlen": W(S=900, H=2, D=128, num_blocks=3, layout="contiguous", cp=3, rank=1,
+                       doc_lens=[100, 350, 450], chunk=300),
+    "zigzag_c128": W(S=1024, H=2, D=128, num_blocks=3, layout="zigzag", cp=4, rank=1),
+    "zigzag_r3_cp8": W(S=2048, H=2, D=128, num_blocks=8, layout="zigzag", cp=8, rank=3),
+    "zigzag_ragged": W(S=900, H=2, D=128, num_blocks=2, layout="zigzag", cp=3, rank=2),
+    "zigzag_d64": W(S=512, H=2, D=64, num_blocks=3, layout="zigzag", cp=2, rank=0),
+    "headshard": W(S=1536, H=2, D=128, num_blocks=4, layout="headshard", cp=4,
+                   doc_lens=[512, 512, 256, 256]),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_parity_small(name):
+    w = CASES[name]
+    say(f"[parity] {name}: {w}")
+    inp = synth.make_inputs(w)
+    hip = run_hip(w, inp)
+    ref = run_oracle(w, inp)
+    m = compare(w, hip, ref)
+    say(f"[parity] {name}: {m}")
+    assert_within(w, m)
+
+
+def test_unseen_keys_get_exact_zero_grads():
+    # zig-zag rank 1 of cp=4: chunks 6 and 7 (after the late chunk 6) are seen by
+    # no local query; contiguous rank 0 of cp=4 sees only the first quarter.
+    for w, unseen in ((W(S=1024, H=2, D=128, num_blocks=3, layout="zigzag", cp=4, rank=1), slice(7 * 128, 1024)),
+                      (W(S=1024, H=2, D=128, num_blocks=2, layout="contiguous", cp=4, rank=0, chunk=256), slice(256, 1024))):
+        inp = synth.make_inputs(w)
+        _, _, (dq, dk0, dv0, dkd, dvd) = run_hip(w, inp)
+        assert torch.count_nonzero(dk0[:, unseen]) == 0
+        assert torch.count_nonzero(dv0[:, unseen]) == 0
+
+
+def test_deterministic_bitwise():
+    w = CASES["bf16_varlen_nb8"]
+    inp = synth.make_inputs(w)
+    a = run_hip(w, inp)
+    b = run_hip(w, inp)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    for x, y in zip(a[2], b[2]):
+        assert torch.equal(x, y)
+
+
+def test_zero_query_closed_form_on_gpu():
+    # q = 0: lse_t = ln(n_t), out_t = mean of the visible values, dk = 0.
+    w = W(S=700, H=2, D=128, num_blocks=4, doc_lens=[300, 400])
+    inp = synth.make_inputs(w)
+    inp["q"].zero_()
+    out, lse, (dq, dk0, dv0, dkd, dvd) = run_hip(w, inp)
+    cu = w.cu_seqlens()
+    start = np.repeat(cu[:-1], w.doc_lens)
+    n = (np.arange(w.T) - start + 1) + w.N
+    np.testing.assert_allclose(lse[0].numpy(), np.broadcast_to(np.log(n), (w.H, w.T)), atol=1e-5)
+    assert torch.count_nonzero(dk0) == 0 and torch.count_nonzero(dkd) == 0
+
+
+def test_lse_merge_kernel_matches_oracle():
+    g = torch.Generator().manual_seed(5)
+    B, T, H, D = 2, 77, 3, 128
+    out = torch.randn(B, T, H, D, generator=g)
+    lse = torch.randn(B, H, T, generator=g) * 3
+    bo = torch.randn(B, T, H, D, generator=g)
+    bl = torch.randn(B, H, T, generator=g) * 3
+    lse[0, 0, :5] = float("-inf")          # empty state rows take the block
+    bl[1, 2, 10:20] = float("-inf")        # empty block rows are no-ops
+    bl[0, 1, 3] = lse[0, 1, 3] + 200.0     # far apart
+    for layout in (0, 1):
+        blk = bl if layout == 0 else bl.permute(0, 2, 1).contiguous()
+        o, l = out.clone().cuda(), lse.clone().cuda()
+        e3.lse_merge(o, l, bo.cuda(), blk.cuda(), block_lse_layout=layout)
+        torch.cuda.synchronize()
+        ro, rl, _ = oracle.lse_merge(out.double().numpy(), lse.double().numpy().transpose(0, 2, 1),
+                                     bo.double().numpy(), bl.double().numpy().transpose(0, 2, 1))
+        np.testing.assert_allclose(o.cpu().numpy(), ro, atol=2e-6, rtol=0)
+        np.testing.assert_allclose(l.cpu().numpy(), rl.transpose(0, 2, 1), atol=2e-6, rtol=0)
+
+
+def test_block0_merged_with_diagonals_by_lse_merge_equals_joint_pass():
+    """Block 0 alone (num_blocks = 1), merged with each diagonal block as a
+    one-key block (out = vd_i, lse = scale <q, kd_i>) by the lse_merge kernel,
+    equals the single joint pass (ring_attention page, `_merge_diag`)."""
+    w = W(dtype="f32", S=512, H=2, D=64, num_blocks=4)
+    inp = synth.make_inputs(w)
+    d = {k: v.cuda() for k, v in inp.items()}
+    prob = e3.Problem(w.B, w.T, w.T_kv, w.H, w.D, w.num_blocks, w.scale, dtype=torch.float32)
+    out, lse = e3.fwd(prob, d["q"], d["k0"], d["v0"], d["kd"], d["vd"])
+    p1 = e3.Problem(w.B, w.T, w.T_kv, w.H, w.D, 1, w.scale, dtype=torch.float32)
+    o0, l0 = e3.fwd(p1, d["q"], d["k0"], d["v0"])
+    for i in range(w.N):
+        bl = (w.scale * (d["q"] * d["kd"][:, i]).sum(-1)).permute(0, 2, 1).contiguous()
+        e3.lse_merge(o0, l0, d["vd"][:, i].contiguous(), bl)
+    torch.cuda.synchronize()
+    assert (o0 - out).abs().max().item() < 1e-5
+    assert (l0 - lse).abs().max().item() < 1e-5

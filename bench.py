@@ -1,0 +1,299 @@
+"""Benchmark of EAGLE-3 mixed attention (forward + backward) on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload dense]
+
+One step = one pass of the whole hot path over one batch: the forward (block-0
+causal attention + TTT diagonals + merge) and the backward (delta, dK/dV, dQ +
+closed-form diagonal gradients). Inputs are seeded synthetic tensors already
+resident in HBM. Prints ONE JSON line with the throughput in TFLOP/s counted
+with causal FLOPs (F_fwd = 4*B*H*D*P0 over the attended block-0 pairs P0,
+F_bwd = 2.5*F_fwd; the diagonal FLOPs are not counted), the per-kernel times
+measured with HIP events on the launch stream, the roofline of the dominant
+kernel and the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "EAGLE-3 mixed attn fwd+bwd TFLOP/s (causal) + % bf16 MFMA peak, T=4096 H=32 D=128"
+PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}   # MI355X dense MFMA (bf16) / fp32 vector
+PEAK_GBS = 8000.0                               # MI355X HBM3E
+KERNELS = ["fwd", "delta", "dkdv", "dq"]
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_work(w, P0):
+    """Algorithmic FLOPs and HBM bytes per launch of each kernel.
+    u = T*H*D*esz (one local [T,H,D] tensor), ukv = T_kv*H*D*esz."""
+    esz = 2 if w.dtype == "bf16" else 4
+    B, T, Tkv, H, D, N = w.B, w.T, w.T_kv, w.H, w.D, w.N
+    u = B * T * H * D * esz
+    ukv = B * Tkv * H * D * esz
+    rowf = B * H * T * 4                      # one float per (b, h, row): lse or delta
+    pf = B * H * D * P0                       # one D-long dot per attended pair
+    diagf = B * H * D * T * N
+    return {
+        # q, k0, v0, kd, vd read; out, lse written
+        "fwd": dict(flop=4 * pf, diag_flop=4 * diagf, bytes=u + 2 * ukv + 2 * N * u + u + rowf),
+        # dO, O read; delta written
+        "delta": dict(flop=0, diag_flop=0, bytes=2 * u + rowf),
+        # q, dO, k0, v0, lse, delta read; dk0, dv0 written; S, dP, dV, dK = 4 GEMMs
+        "dkdv": dict(flop=8 * pf, diag_flop=0, bytes=2 * u + 4 * ukv + 2 * rowf),
+        # q, dO, k0, v0, lse, delta, kd, vd read; dq, dkd, dvd written; S, dP, dQ = 3 GEMMs
+        "dq": dict(flop=6 * pf, diag_flop=10 * diagf, bytes=3 * u + 2 * ukv + 4 * N * u + 2 * rowf),
+    }
+
+
+class HipEvents:
+    """hipEvent_t handles from the HIP runtime torch already loaded."""
+
+    def __init__(self):
+        self.rt = ctypes.CDLL("libamdhip64.so.7")
+        self.rt.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                ctypes.c_void_p]
+        self.rt.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.rt.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+
+    def create(self, n):
+        arr = (ctypes.c_void_p * n)()
+        for i in range(n):
+            e = ctypes.c_void_p()
+            rc = self.rt.hipEventCreate(ctypes.byref(e))
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreate failed: {rc}")
+            arr[i] = e.value
+        return arr
+
+    def elapsed_ms(self, a, b):
+        t = ctypes.c_float()
+        rc = self.rt.hipEventElapsedTime(ctypes.byref(t), ctypes.c_void_p(a), ctypes.c_void_p(b))
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed: {rc}")
+        return float(t.value)
+
+    def destroy(self, arr):
+        for e in arr:
+            self.rt.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def cpu_baseline(w, inp, P0_per_head, budget_s):
+    """The CPU oracle (float64) on whole heads of the same workload until about
+    `budget_s` seconds of work; throughput on the same counted FLOPs."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = None
+    f = {k: v.double().numpy() for k, v in inp.items()}
+    cu = w.cu_seqlens()
+    ocp = w.cp if w.layout in ("contiguous", "zigzag") else 1
+    done, secs = 0, 0.0
+    for h in range(w.H):
+        t0 = time.perf_counter()
+        out, lse = oracle.forward(f["q"], f["k0"], f["v0"], f["kd"], f["vd"], w.scale, cu,
+                                  w.layout, ocp, w.rank, heads=[h])
+        oracle.backward(f["dout"], f["q"], f["k0"], f["v0"], f["kd"], f["vd"], w.scale, cu,
+                        w.layout, ocp, w.rank, out=out, lse=lse, heads=[h])
+        secs += time.perf_counter() - t0
+        done += 1
+        if secs >= budget_s:
+            break
+    flop = 3.5 * 4 * w.B * w.D * P0_per_head * done
+    cores = len(os.sched_getaffinity(0))
+    return {
+        "value": flop / secs / 1e12, "unit": "TFLOP/s", "cores": blas_threads or cores,
+        "kind": "oracle",
+        "sample": f"{done} of {w.H} heads (all {w.T} rows, fwd+bwd, float64 NumPy), "
+                  f"{secs:.1f} s; host has {cores} cores available",
+        "seconds": secs,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="dense")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="seconds of CPU oracle work for the baseline (0 = skip)")
+    ap.add_argument("--no-flush", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU's share on one GPU only; --gpus {args.gpus} "
+              f"(WORLD_SIZE={world}) is not supported: the multi-GPU path is not built "
+              "(collectives are out of scope for this build).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import eagle_draft_amd as e3
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = synth.workload(args.workload, seed=args.seed)
+    log(f"[bench] workload {w}")
+    inp_cpu = synth.make_inputs(w)
+    d = {k: v.to(dev) for k, v in inp_cpu.items()}
+    prob = e3.Problem(w.B, w.T, w.T_kv, w.H, w.D, w.num_blocks, w.scale, dtype=w.torch_dtype,
+                      layout=w.layout, cp=w.cp, rank=w.rank, cu_seqlens=w.cu_seqlens(), device=dev)
+    P0 = prob.pair_count()                      # per (batch row, head)
+    out = torch.empty_like(d["q"])
+    lse = torch.empty(w.B, w.H, w.T, dtype=torch.float32, device=dev)
+    grads = (torch.empty_like(d["q"]), torch.empty_like(d["k0"]), torch.empty_like(d["v0"]),
+             torch.empty_like(d["kd"]), torch.empty_like(d["vd"]))
+    ws = torch.empty(max(prob.workspace_bytes(), 256), dtype=torch.uint8, device=dev)
+    lib = e3.lib()
+
+    def step():
+        e3.fwd(prob, d["q"], d["k0"], d["v0"], d["kd"], d["vd"], out=out, lse=lse)
+        e3.bwd(prob, d["dout"], d["q"], d["k0"], d["v0"], d["kd"], d["vd"], out, lse,
+               grads=grads, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {args.warmup} done")
+
+    # (1) the timed region: exactly K back-to-back steps, synchronized on both sides
+    ev = HipEvents()
+    se = ev.create(2)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    ev.rt.hipEventRecord(ctypes.c_void_p(se[0]), stream)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    ev.rt.hipEventRecord(ctypes.c_void_p(se[1]), stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    total_ms = ev.elapsed_ms(se[0], se[1])
+    ms_per_step = total_ms / args.steps
+    log(f"[bench] {args.steps} steps: {total_ms:.3f} ms ({ms_per_step:.4f} ms/step, wall {wall_ms:.1f} ms)")
+
+    # (2) per-kernel times: events recorded by the library around each kernel
+    nfwd, nbwd = 2, 4
+    per = {k: [] for k in KERNELS}
+    fwd_ms, bwd_ms, flushed = [], [], []
+    flush_buf = None if args.no_flush else torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    reps = max(args.steps, 5)
+    evf = ev.create(nfwd * reps)
+    evb = ev.create(nbwd * reps)
+    for r in range(reps):
+        if flush_buf is not None:
+            flush_buf.zero_()     # evict L2 and MALL between steps (outside the events)
+        psz = ctypes.sizeof(ctypes.c_void_p)
+        lib.eagle3_set_timing_events(ctypes.c_void_p(ctypes.addressof(evf) + r * nfwd * psz), nfwd)
+        e3.fwd(prob, d["q"], d["k0"], d["v0"], d["kd"], d["vd"], out=out, lse=lse)
+        assert lib.eagle3_timing_events_recorded() == nfwd
+        lib.eagle3_set_timing_events(ctypes.c_void_p(ctypes.addressof(evb) + r * nbwd * psz), nbwd)
+        e3.bwd(prob, d["dout"], d["q"], d["k0"], d["v0"], d["kd"], d["vd"], out, lse,
+               grads=grads, workspace=ws)
+        assert lib.eagle3_timing_events_recorded() == nbwd
+        lib.eagle3_set_timing_events(None, 0)
+    torch.cuda.synchronize()
+    for r in range(reps):
+        f0 = r * nfwd
+        b0 = r * nbwd
+        per["fwd"].append(ev.elapsed_ms(evf[f0], evf[f0 + 1]))
+        per["delta"].append(ev.elapsed_ms(evb[b0], evb[b0 + 1]))
+        per["dkdv"].append(ev.elapsed_ms(evb[b0 + 1], evb[b0 + 2]))
+        per["dq"].append(ev.elapsed_ms(evb[b0 + 2], evb[b0 + 3]))
+        fwd_ms.append(per["fwd"][-1])
+        bwd_ms.append(ev.elapsed_ms(evb[b0], evb[b0 + 3]))
+        flushed.append(fwd_ms[-1] + bwd_ms[-1])
+    ev.destroy(se)
+    ev.destroy(evf)
+    ev.destroy(evb)
+    del flush_buf
+
+    work = kernel_work(w, P0)
+    kern = {}
+    for k in KERNELS:
+        t_us = statistics.mean(per[k]) * 1e3
+        kw = work[k]
+        kern[k] = {
+            "us_mean": round(t_us, 2), "us_median": round(statistics.median(per[k]) * 1e3, 2),
+            "tflops": round(kw["flop"] / (t_us * 1e-6) / 1e12, 2) if kw["flop"] else 0.0,
+            "gbs": round(kw["bytes"] / (t_us * 1e-6) / 1e9, 1),
+            "flop": kw["flop"], "bytes": kw["bytes"],
+        }
+    dom = max(KERNELS, key=lambda k: kern[k]["us_mean"])
+    dk = kern[dom]
+    t_dom = dk["us_mean"] * 1e-6
+    peak_t = PEAK_TFLOPS[w.dtype]
+    mfma_time = dk["flop"] / (peak_t * 1e12)
+    hbm_time = dk["bytes"] / (PEAK_GBS * 1e9)
+    if mfma_time >= hbm_time and dk["flop"] > 0:
+        roof = {"bound": "mfma", "achieved": round(dk["flop"] / t_dom / 1e12, 2), "peak": peak_t,
+                "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": round(dk["bytes"] / t_dom / 1e9, 1), "peak": PEAK_GBS,
+                "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = None
+    roof["kernel"] = dom
+    roof["algorithmic"] = {"flop": dk["flop"], "bytes": dk["bytes"]}
+
+    counted = 3.5 * 4 * w.B * w.H * w.D * P0
+    value = counted / (ms_per_step * 1e-3) / 1e12
+    props = torch.cuda.get_device_properties(dev)
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) inputs, resident in HBM)",
+        "config": {"workload": w.name, "B": w.B, "T": w.T, "T_kv": w.T_kv, "H": w.H, "D": w.D,
+                   "num_blocks": w.num_blocks, "layout": w.layout, "cp": w.cp, "rank": w.rank,
+                   "num_docs": len(w.doc_lens) if w.doc_lens else 1, "seed": w.seed},
+        "pct_peak": round(100.0 * value / PEAK_TFLOPS[w.dtype], 2),
+        "counted_flop": counted,
+        "pairs_P0": P0,
+        "flushed_ms_per_step_median": round(statistics.median(flushed), 4),
+        "fwd_ms_median": round(statistics.median(fwd_ms), 4),
+        "bwd_ms_median": round(statistics.median(bwd_ms), 4),
+        "kernels": kern,
+        "roofline": roof,
+        "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
+                   "compute_units": props.multi_processor_count},
+    }
+    if args.cpu_budget > 0:
+        log("[bench] timing the CPU oracle ...")
+        res["cpu_baseline"] = cpu_baseline(w, inp_cpu, P0, args.cpu_budget)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -91,6 +91,9 @@ def _load():
     lib.eagle3_fwd_tile_segments.argtypes = [P, ctypes.c_int, ctypes.POINTER(ctypes.c_int32),
                                              ctypes.POINTER(ctypes.c_int32), ctypes.c_int]
     lib.eagle3_fwd_tile_segments.restype = ctypes.c_int
+    lib.eagle3_set_timing_events.argtypes = [vp, ctypes.c_int]
+    lib.eagle3_set_timing_events.restype = ctypes.c_int
+    lib.eagle3_timing_events_recorded.restype = ctypes.c_int
     v = lib.eagle3_abi_version()
     if v != ABI_VERSION:
         raise RuntimeError(f"libeagle3_attn ABI version {v} != binding version {ABI_VERSION}")

@@ -25,6 +25,11 @@ int fwd_tile_keys();
 namespace {
 
 thread_local std::string g_err;
+thread_local hipEvent_t* g_events = nullptr;
+thread_local int g_events_cap = 0;
+thread_local int g_events_n = 0;
+
+void timing_reset() { g_events_n = 0; }
 
 int fail(int code, const char* fmt, ...) {
   char buf[512];
@@ -161,6 +166,7 @@ int fwd_impl(const e3_problem* p, const void* q, const void* k0, const void* v0,
     const void* ptrs[] = {kd, vd};
     if ((rc = check_ptrs(names, ptrs, 2))) return rc;
   }
+  timing_reset();
   e3::Args a = make_args(p, r);
   a.q = q;
   a.k0 = k0;
@@ -191,6 +197,7 @@ int bwd_impl(const e3_problem* p, const void* dout, const void* q, const void* k
     const void* ptrs[] = {kd, vd, dkd, dvd};
     if ((rc = check_ptrs(names, ptrs, 4))) return rc;
   }
+  timing_reset();
   e3::Args a = make_args(p, r);
   a.q = q;
   a.k0 = k0;
@@ -219,7 +226,20 @@ int doc_lo_host(const e3_problem* p, int pos) {
 
 }  // namespace
 
+void e3::timing_mark(hipStream_t st) {
+  if (g_events && g_events_n < g_events_cap) (void)hipEventRecord(g_events[g_events_n++], st);
+}
+
 extern "C" {
+
+int eagle3_set_timing_events(hipEvent_t* events, int capacity) {
+  g_events = capacity > 0 ? events : nullptr;
+  g_events_cap = events ? capacity : 0;
+  g_events_n = 0;
+  return E3_OK;
+}
+
+int eagle3_timing_events_recorded(void) { return g_events_n; }
 
 int eagle3_abi_version(void) { return EAGLE3_ABI_VERSION; }
 

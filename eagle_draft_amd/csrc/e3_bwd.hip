@@ -467,15 +467,18 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const Args a) {
 template <typename T, int D>
 static hipError_t launch_bwd_t(const Args& a, hipStream_t st) {
   const long long nrow = (long long)a.B * a.T * a.H;
+  timing_mark(st);
   if (nrow > 0) {
     const long long nb = (nrow + (256 / (D / 8)) - 1) / (256 / (D / 8));
     hipLaunchKernelGGL((delta_kernel<T, D>), dim3((unsigned)nb), dim3(256), 0, st, a);
+    timing_mark(st);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   const long long nk = (long long)((a.Tkv + DkdvCfg<T, D>::BNK - 1) / DkdvCfg<T, D>::BNK) * a.B * a.H;
   if (nk > 0) {
     hipLaunchKernelGGL((dkdv_kernel<T, D>), dim3((unsigned)nk), dim3(256), 0, st, a);
+    timing_mark(st);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -483,6 +486,7 @@ static hipError_t launch_bwd_t(const Args& a, hipStream_t st) {
   const long long nq = (long long)geo.ntiles(DqCfg<T, D>::BM) * a.B * a.H;
   if (nq > 0) {
     hipLaunchKernelGGL((dq_kernel<T, D>), dim3((unsigned)nq), dim3(256), 0, st, a);
+    timing_mark(st);
     return hipGetLastError();
   }
   return hipSuccess;

@@ -49,6 +49,10 @@ struct Args {
   int layout, cp, rank;
 };
 
+// Measurement hook (host): records the next caller-provided timing event, if any,
+// on the stream. Called before the first kernel of an entry point and after each.
+void timing_mark(hipStream_t st);
+
 // ---------------------------------------------------------------------------
 // Share geometry (host and device)
 // ---------------------------------------------------------------------------

@@ -244,7 +244,9 @@ static hipError_t launch_fwd_t(const Args& a, hipStream_t st) {
   const Geo geo{a.layout, a.cp, a.rank, a.T, a.Tkv};
   const long long nt = (long long)geo.ntiles(FwdCfg<T, D>::BM) * a.B * a.H;
   if (nt == 0) return hipSuccess;
+  timing_mark(st);
   hipLaunchKernelGGL((fwd_kernel<T, D>), dim3((unsigned)nt), dim3(256), 0, st, a);
+  timing_mark(st);
   return hipGetLastError();
 }
 

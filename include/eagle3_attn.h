@@ -157,6 +157,17 @@ int eagle3_shard_bwd(const e3_problem* p, const void* dout, const void* q, const
 int lse_merge(float* out, float* lse, const float* block_out, const float* block_lse,
               int B, int T, int H, int D, int block_lse_layout, hipStream_t stream);
 
+/* ---- Measurement hook ---------------------------------------------------------------- */
+
+/* While `events` is non-NULL, every compute entry point called on this thread records
+ * events[0] on its stream before its first kernel and events[k+1] after its k-th kernel
+ * (at most `capacity` events; the forward launches 1 kernel, the backward 3: delta, dK/dV,
+ * dQ). The caller creates and owns the events; NULL stops recording. Returns E3_OK. */
+int eagle3_set_timing_events(hipEvent_t* events, int capacity);
+
+/* Number of events recorded by the last compute entry point called on this thread. */
+int eagle3_timing_events_recorded(void);
+
 /* ---- Host-only inspection of the shard driver (no GPU needed) ---------------------- */
 
 /* Global sequence position of every local query row: pos_host[T] (HOST memory). */

@@ -54,12 +54,11 @@ template <typename T, int D>
 struct DkdvCfg {
   static constexpr int BNK = 128;            // keys per workgroup (32 per wave)
   static constexpr int BMQ = 64;             // query rows per iteration
-  static constexpr int PAD = 16 / (int)sizeof(T);
-  static constexpr int NSTR = D + PAD;       // natural Q / dO rows
-  static constexpr int TSTR = BMQ + PAD;     // transposed Q / dO rows
+  static constexpr int STR = Stride<T, D>::both;   // Q and dO tiles are read both ways
   static constexpr int KS = D / 16;
   static constexpr int DB = D / 32;
-  static constexpr int LDS = (2 * BMQ * NSTR + 2 * D * TSTR) * (int)sizeof(T) + 2 * BMQ * 4;
+  static constexpr int STAGE = 2 * BMQ * STR * (int)sizeof(T) + 2 * BMQ * 4;
+  static constexpr int LDS = 2 * STAGE;
 };
 
 // Query tiles (rows of the share) that can see keys [k_lo, k_hi) with document
@@ -105,14 +104,11 @@ template <typename T, int D>
 __global__ __launch_bounds__(256, 1) void dkdv_kernel(const Args a) {
   using C = DkdvCfg<T, D>;
   using Op = typename V8<T>::type;
-  constexpr int BNK = C::BNK, BMQ = C::BMQ, KS = C::KS, DB = C::DB;
+  constexpr int BNK = C::BNK, BMQ = C::BMQ, KS = C::KS, DB = C::DB, STR = C::STR;
   __shared__ __attribute__((aligned(16))) char smem[C::LDS];
-  T* Qs = reinterpret_cast<T*>(smem);
-  T* Os = Qs + BMQ * C::NSTR;
-  T* Qt = Os + BMQ * C::NSTR;
-  T* Ot = Qt + D * C::TSTR;
-  float* L2s = reinterpret_cast<float*>(Ot + D * C::TSTR);
-  float* Ds = L2s + BMQ;
+  auto qbuf = [&](int s) { return reinterpret_cast<T*>(smem + s * C::STAGE); };
+  auto obuf = [&](int s) { return reinterpret_cast<T*>(smem + s * C::STAGE) + BMQ * STR; };
+  auto lbuf = [&](int s) { return reinterpret_cast<float*>(smem + s * C::STAGE + 2 * BMQ * STR * (int)sizeof(T)); };
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
   const int BH = a.B * a.H;
@@ -156,30 +152,44 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const Args a) {
   it.begin(geo, kt0, q_hi, BMQ);
   TileLoad<T, BMQ, D, 256> qt, ot;
   float lv = 0.f, dl = 0.f;
-  auto prefetch = [&]() {
-    const int r0 = it.row0(), nr = it.nrows(BMQ);
-    qt.load(qb + (long long)r0 * rs, rs, nr, tid);
-    ot.load(dob + (long long)r0 * rs, rs, nr, tid);
+  auto fetch = [&](const QIter& q) {
+    const int r0 = q.row0(), nr = q.nrows(BMQ);
+    if (nr == BMQ) {
+      qt.load_full(qb + (long long)r0 * rs, rs, tid);
+      ot.load_full(dob + (long long)r0 * rs, rs, tid);
+    } else {
+      qt.load(qb + (long long)r0 * rs, rs, nr, tid);
+      ot.load(dob + (long long)r0 * rs, rs, nr, tid);
+    }
     if (tid < BMQ) {
       lv = tid < nr ? lseb[r0 + tid] * kLog2e : 0.f;
       dl = tid < nr ? delb[r0 + tid] : 0.f;
     }
   };
-  if (it.valid) prefetch();
+  auto put = [&](int st) {
+    qt.store(qbuf(st), STR, tid);
+    ot.store(obuf(st), STR, tid);
+    if (tid < BMQ) {
+      lbuf(st)[tid] = lv;
+      lbuf(st)[BMQ + tid] = dl;
+    }
+  };
+  int stage = 0;
+  if (it.valid) {
+    fetch(it);
+    put(0);
+  }
+  QIter nx = it;
+  if (nx.valid) nx.next(geo, BMQ);
+  if (nx.valid) fetch(nx);
+  __syncthreads();
+
   while (it.valid) {
     const int nr = it.nrows(BMQ), gq0 = it.gpos0();
-    __syncthreads();
-    qt.store_nat(Qs, C::NSTR, tid);
-    qt.store_tr(Qt, C::TSTR, tid);
-    ot.store_nat(Os, C::NSTR, tid);
-    ot.store_tr(Ot, C::TSTR, tid);
-    if (tid < BMQ) {
-      L2s[tid] = lv;
-      Ds[tid] = dl;
-    }
-    __syncthreads();
-    it.next(geo, BMQ);
-    if (it.valid) prefetch();
+    const T* Qs = qbuf(stage);
+    const T* Os = obuf(stage);
+    const float* L2s = lbuf(stage);
+    const float* Ds = L2s + BMQ;
 
     // S = Q K^T and dP = dO V^T: two 32-query blocks, lane = key, 16 queries each.
     f32x16 sp[2], dp[2];
@@ -192,10 +202,8 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const Args a) {
       }
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const Op qa = load8(Qs + (32 * mb + l32) * C::NSTR + 16 * ks + 8 * g);
-        mfma16(qa, kreg[ks], sp[mb]);
-        const Op oa = load8(Os + (32 * mb + l32) * C::NSTR + 16 * ks + 8 * g);
-        mfma16(oa, vreg[ks], dp[mb]);
+        mfma16(lds_row8(Qs, STR, 32 * mb + l32, 16 * ks + 8 * g), kreg[ks], sp[mb]);
+        mfma16(lds_row8(Os, STR, 32 * mb + l32, 16 * ks + 8 * g), vreg[ks], dp[mb]);
       }
     }
     const bool interior = nr == BMQ && kt0 + BNK <= a.Tkv && gq0 >= kt0 + BNK - 1 &&
@@ -210,7 +218,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const Args a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int j = 4 * jj + i;
-          float p = fast_exp2(sp[mb][j] * c2 - l4[i]);
+          float p = fast_exp2(fmaf(sp[mb][j], c2, -l4[i]));
           if (!interior) {
             const int m = m0 + i, gm = gq0 + m;
             const bool vis = svalid && m < nr && gm >= s && gm < s_hi;
@@ -227,12 +235,19 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const Args a) {
       const Op sb = to_op(dp[ks >> 1], 8 * (ks & 1), T());
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const Op oa = load8(Ot + (32 * db + l32) * C::TSTR + 16 * ks + 8 * g);
-        mfma16(oa, pb, dv[db]);
-        const Op qa = load8(Qt + (32 * db + l32) * C::TSTR + 16 * ks + 8 * g);
-        mfma16(qa, sb, dk[db]);
+        mfma16(lds_col8(Os, STR, 16 * ks, 32 * db, lane), pb, dv[db]);
+        mfma16(lds_col8(Qs, STR, 16 * ks, 32 * db, lane), sb, dk[db]);
       }
     }
+
+    it = nx;
+    if (it.valid) {
+      put(stage ^ 1);
+      nx.next(geo, BMQ);
+      if (nx.valid) fetch(nx);
+    }
+    stage ^= 1;
+    __syncthreads();
   }
 
   // Write dK0 = scale * dK, dV0 (rows of keys no query sees are zeros).
@@ -264,15 +279,16 @@ template <typename T, int D>
 struct DqCfg {
   static constexpr int BM = 128;
   static constexpr int BN = 64;
-  static constexpr int PAD = 16 / (int)sizeof(T);
-  static constexpr int NSTR = D + PAD;
-  static constexpr int TSTR = BN + PAD;
+  static constexpr int KSTR = Stride<T, D>::both;  // K is read both ways
+  static constexpr int VSTR = Stride<T, D>::nat;
   static constexpr int OSTR = D + 4;
   static constexpr int KS = D / 16;
   static constexpr int DB = D / 32;
-  static constexpr int LDS_KV = (2 * BN * NSTR + D * TSTR) * (int)sizeof(T);
+  static constexpr int STAGE = (BN * KSTR + BN * VSTR) * (int)sizeof(T);
+  static constexpr int LDS_KV = 2 * STAGE;
   static constexpr int LDS_EPI = 4 * 32 * OSTR * 4;
   static constexpr int LDS = LDS_KV > LDS_EPI ? LDS_KV : LDS_EPI;
+  static constexpr int NB = 4;              // diagonal blocks per epilogue group
 };
 
 template <typename T, int D>
@@ -281,9 +297,8 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const Args a) {
   using Op = typename V8<T>::type;
   constexpr int BM = C::BM, BN = C::BN, KS = C::KS, DB = C::DB;
   __shared__ __attribute__((aligned(16))) char smem[C::LDS];
-  T* Ks = reinterpret_cast<T*>(smem);
-  T* Vs = Ks + BN * C::NSTR;
-  T* Kt = Vs + BN * C::NSTR;
+  auto kbuf = [&](int s) { return reinterpret_cast<T*>(smem + s * C::STAGE); };
+  auto vbuf = [&](int s) { return reinterpret_cast<T*>(smem + s * C::STAGE) + BN * C::KSTR; };
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
   const int BH = a.B * a.H;
@@ -327,67 +342,80 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const Args a) {
   SegIter it;
   it.begin(geo, lo_min, g_max + 1, BN);
   TileLoad<T, BN, D, 256> kt, vt;
+  auto fetch = [&](int s0) {
+    const int nv = a.Tkv - s0;
+    if (nv >= BN) {
+      kt.load_full(k0b + (long long)s0 * rs, rs, tid);
+      vt.load_full(v0b + (long long)s0 * rs, rs, tid);
+    } else {
+      kt.load(k0b + (long long)s0 * rs, rs, nv, tid);
+      vt.load(v0b + (long long)s0 * rs, rs, nv, tid);
+    }
+  };
+  int stage = 0;
   if (it.valid) {
-    const int nv = a.Tkv - it.s0;
-    kt.load(k0b + (long long)it.s0 * rs, rs, nv, tid);
-    vt.load(v0b + (long long)it.s0 * rs, rs, nv, tid);
+    fetch(it.s0);
+    kt.store(kbuf(0), C::KSTR, tid);
+    vt.store(vbuf(0), C::VSTR, tid);
   }
+  SegIter nx = it;
+  if (nx.valid) nx.next(geo, BN);
+  if (nx.valid) fetch(nx.s0);
+  __syncthreads();
+
   while (it.valid) {
     const int s0 = it.s0, sa = it.a, sb = it.b;
-    __syncthreads();
-    kt.store_nat(Ks, C::NSTR, tid);
-    kt.store_tr(Kt, C::TSTR, tid);
-    vt.store_nat(Vs, C::NSTR, tid);
-    __syncthreads();
-    it.next(geo, BN);
-    if (it.valid) {
-      const int nv = a.Tkv - it.s0;
-      kt.load(k0b + (long long)it.s0 * rs, rs, nv, tid);
-      vt.load(v0b + (long long)it.s0 * rs, rs, nv, tid);
-    }
+    const T* Ks = kbuf(stage);
+    const T* Vs = vbuf(stage);
 
-    f32x16 st[2], dpt[2];
+    // One 32-key block at a time: S^T, dP^T, then dS^T as two MFMA operands.
+    const bool interior = s0 >= sa && s0 + BN <= sb && s0 >= lo_max && s0 + BN - 1 <= g_min;
+    Op dsop[BN / 16];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
+      f32x16 st, dpt;
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        st[kb][j] = 0.f;
-        dpt[kb][j] = 0.f;
+        st[j] = 0.f;
+        dpt[j] = 0.f;
       }
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const Op ka = load8(Ks + (32 * kb + l32) * C::NSTR + 16 * ks + 8 * g);
-        mfma16(ka, qreg[ks], st[kb]);
-        const Op va = load8(Vs + (32 * kb + l32) * C::NSTR + 16 * ks + 8 * g);
-        mfma16(va, oreg[ks], dpt[kb]);
+        mfma16(lds_row8(Ks, C::KSTR, 32 * kb + l32, 16 * ks + 8 * g), qreg[ks], st);
+        mfma16(lds_row8(Vs, C::VSTR, 32 * kb + l32, 16 * ks + 8 * g), oreg[ks], dpt);
       }
-    }
-    const bool interior = s0 >= sa && s0 + BN <= sb && s0 >= lo_max && s0 + BN - 1 <= g_min;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        float p = fast_exp2(st[kb][j] * c2 - lq);
+        float p = fast_exp2(fmaf(st[j], c2, -lq));
         if (!interior) {
           const int s = s0 + 32 * kb + 8 * (j >> 2) + 4 * g + (j & 3);
           const bool vis = s >= sa && s < sb && s >= loq && s <= gq;
           p = vis ? p : 0.f;
         }
-        dpt[kb][j] = p * (dpt[kb][j] - dq_delta);
+        dpt[j] = p * (dpt[j] - dq_delta);
       }
-#pragma unroll
-    for (int ks = 0; ks < BN / 16; ++ks) {
-      const Op sbv = to_op(dpt[ks >> 1], 8 * (ks & 1), T());
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const Op ka = load8(Kt + (32 * db + l32) * C::TSTR + 16 * ks + 8 * g);
-        mfma16(ka, sbv, acc[db]);
-      }
+      dsop[2 * kb] = to_op(dpt, 0, T());
+      dsop[2 * kb + 1] = to_op(dpt, 8, T());
     }
+    // dQ^T += K^T dS^T over the 64 keys (4 k-steps of 16).
+#pragma unroll
+    for (int ks = 0; ks < BN / 16; ++ks)
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        mfma16(lds_col8(Ks, C::KSTR, 16 * ks, 32 * db, lane), dsop[ks], acc[db]);
+
+    it = nx;
+    if (it.valid) {
+      kt.store(kbuf(stage ^ 1), C::KSTR, tid);
+      vt.store(vbuf(stage ^ 1), C::VSTR, tid);
+      nx.next(geo, BN);
+      if (nx.valid) fetch(nx.s0);
+    }
+    stage ^= 1;
+    __syncthreads();
   }
 
   // ---- epilogue: stage dQ^T through LDS, then the diagonal terms row-major ----
-  __syncthreads();
   float* Qw = reinterpret_cast<float*>(smem) + w * 32 * C::OSTR;
 #pragma unroll
   for (int db = 0; db < DB; ++db)
@@ -404,6 +432,7 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const Args a) {
 
   constexpr int LPR = D / 8;
   constexpr int RPP = 64 / LPR;
+  constexpr int NB = C::NB;
   const int lr = lane / LPR, cc = (lane % LPR) * 8;
   const T* kdb = reinterpret_cast<const T*>(a.kd) + (long long)b * a.kd_bs + (long long)h * D + cc;
   const T* vdb = reinterpret_cast<const T*>(a.vd) + (long long)b * a.kd_bs + (long long)h * D + cc;
@@ -414,32 +443,31 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const Args a) {
   for (int pass = 0; pass < 32 / RPP; ++pass) {
     const int rr = pass * RPP + lr;
     const int tr = w * 32 + rr;
-    if (tr >= nrows) continue;
-    const long long row = row0 + tr;
+    const bool ok = tr < nrows;              // whole row groups agree
+    const long long row = row0 + (ok ? tr : 0);
     f32x8 dqv = *reinterpret_cast<const f32x8*>(Qw + rr * C::OSTR + cc);
     const f32x8 qv = load8f(qb + row * rs + cc);
     const f32x8 ov = load8f(dob + row * rs + cc);
     const float l2 = lseb[row] * kLog2e;
     const float dl = delb[row];
-    for (int i0 = 0; i0 < a.N; i0 += 4) {
-      const int n = (a.N - i0) < 4 ? (a.N - i0) : 4;
-      f32x8 kv[4], vv[4];
+    for (int i0 = 0; i0 < a.N; i0 += NB) {
+      const int n = (a.N - i0) < NB ? (a.N - i0) : NB;
+      typename V8<T>::type kv[NB], vv[NB];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < NB; ++i)
         if (i < n) {
           const long long off = (long long)(i0 + i) * a.kd_blk + row * rs;
-          kv[i] = load8f(kdb + off);
-          vv[i] = load8f(vdb + off);
+          kv[i] = load8(kdb + off);
+          vv[i] = load8(vdb + off);
         }
-      }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < NB; ++i)
         if (i < n) {
           float y = 0.f, dpi = 0.f;
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            y += qv[e] * kv[i][e];
-            dpi += ov[e] * vv[i][e];
+            y += qv[e] * (float)kv[i][e];
+            dpi += ov[e] * (float)vv[i][e];
           }
           y = group_sum<LPR>(y);
           dpi = group_sum<LPR>(dpi);
@@ -448,19 +476,22 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const Args a) {
           f32x8 gk, gv;
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            dqv[e] += ds * kv[i][e];
+            dqv[e] += ds * (float)kv[i][e];
             gk[e] = scale * ds * qv[e];
             gv[e] = pi * ov[e];
           }
-          const long long off = (long long)(i0 + i) * a.kd_blk + row * rs;
-          store8f(dkdb + off, gk);
-          store8f(dvdb + off, gv);
+          if (ok) {
+            const long long off = (long long)(i0 + i) * a.kd_blk + row * rs;
+            store8f(dkdb + off, gk);
+            store8f(dvdb + off, gv);
+          }
         }
-      }
     }
+    if (ok) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) dqv[e] *= scale;
-    store8f(dqb + row * rs, dqv);
+      for (int e = 0; e < 8; ++e) dqv[e] *= scale;
+      store8f(dqb + row * rs, dqv);
+    }
   }
 }
 

@@ -285,12 +285,10 @@ __device__ __forceinline__ void store8f(T* p, const f32x8& v) {
 }
 
 // ---------------------------------------------------------------------------
-// Global -> LDS tile staging. A tile is R rows x D columns of T; thread t holds
-// 4 consecutive rows x E columns. The natural copy keeps [row][col]; the
-// transposed copy is [col][row] with the rows of each 16-row group stored in
-// the order {0-3, 8-11, 4-7, 12-15}, so that an MFMA operand read of 8
-// consecutive elements at offset 8g of a group yields rows {4g..4g+3,
-// 8+4g..8+4g+3}: the row order in which a 32x32 accumulator holds its rows.
+// Global -> LDS tile staging. A tile is R rows x D columns of T kept in LDS in
+// its natural [row][col] layout (row stride chosen per tile to spread banks);
+// thread t holds 4 consecutive rows x E columns in registers between the global
+// load and the LDS store.
 // ---------------------------------------------------------------------------
 template <typename T, int E>
 struct VecE {
@@ -303,7 +301,6 @@ struct TileLoad {
   static_assert(E >= 1 && (E & (E - 1)) == 0, "tile does not split evenly");
   static constexpr int CPR = D / E;       // column chunks per row
   typedef typename VecE<T, E>::type vec;
-  typedef typename VecE<T, 4>::type vec4;
   vec r[4];
 
   // rows [row0, row0+R) of a [rows, H*D] tensor (row stride rs); rows at or past
@@ -321,27 +318,73 @@ struct TileLoad {
       }
     }
   }
-  __device__ __forceinline__ void store_nat(T* lds, int stride, int tid) const {
+  // Unguarded: all R rows exist.
+  __device__ __forceinline__ void load_full(const T* base, long long rs, int tid) {
+    const int cc = tid % CPR, rg = tid / CPR;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      r[i] = *reinterpret_cast<const vec*>(base + (long long)(rg * 4 + i) * rs + cc * E);
+  }
+  __device__ __forceinline__ void store(T* lds, int stride, int tid) const {
     const int cc = tid % CPR, rg = tid / CPR;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       *reinterpret_cast<vec*>(lds + (rg * 4 + i) * stride + cc * E) = r[i];
   }
-  __device__ __forceinline__ void store_tr(T* lds, int stride, int tid) const {
-    const int cc = tid % CPR, rg = tid / CPR;
-    const int a = rg & 3;
-    const int slot = ((a & 1) << 1) | (a >> 1);
-    const int col = (rg >> 2) * 16 + slot * 4;
+};
+
+// MFMA operand of 8 consecutive columns of row `row` of a natural tile: A[m][k]
+// with m = row, k = col..col+7 (one 16-byte LDS read for bf16).
+template <typename T>
+__device__ __forceinline__ typename V8<T>::type lds_row8(const T* tile, int stride, int row, int col) {
+  return *reinterpret_cast<const typename V8<T>::type*>(tile + row * stride + col);
+}
+
+// MFMA operand taken down the rows of a natural tile X[k][m]: the lane (m = l%32,
+// g = l/32) gets X[k0 + {4g..4g+3, 8+4g..8+4g+3}][c0 + l%32], the row order in which
+// a 32x32 accumulator holds its rows (so an accumulator slice is the other operand).
+// bf16: two ds_read_b64_tr_b16. In each 16-lane group, source lane j reads the 4
+// columns c + 4(j%4) .. +3 of row k + j/4 and lane i receives column c + i of the
+// 4 rows.
+__device__ __forceinline__ bf16x8 lds_col8(const bf16* tile, int stride, int k0, int c0, int lane) {
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) v4s lv4s;
+  const int g = lane >> 5;
+  const int j = lane & 15;
+  const int col = c0 + 16 * ((lane >> 4) & 1) + 4 * (j & 3);
+  const int row = k0 + 4 * g + (j >> 2);
+  const v4s a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lv4s*)(tile + row * stride + col));
+  const v4s b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lv4s*)(tile + (row + 8) * stride + col));
+  bf16x8 r;
+  const bf16x4 ra = __builtin_bit_cast(bf16x4, a);
+  const bf16x4 rb = __builtin_bit_cast(bf16x4, b);
+  r[0] = ra[0]; r[1] = ra[1]; r[2] = ra[2]; r[3] = ra[3];
+  r[4] = rb[0]; r[5] = rb[1]; r[6] = rb[2]; r[7] = rb[3];
+  return r;
+}
+// fp32: eight scalar LDS reads (no transposing read exists for 32-bit elements).
+__device__ __forceinline__ f32x8 lds_col8(const float* tile, int stride, int k0, int c0, int lane) {
+  const int g = lane >> 5;
+  const int col = c0 + (lane & 31);
+  f32x8 r;
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      vec4 v;
-      v[0] = r[0][e];
-      v[1] = r[1][e];
-      v[2] = r[2][e];
-      v[3] = r[3][e];
-      *reinterpret_cast<vec4*>(lds + (cc * E + e) * stride + col) = v;
-    }
+  for (int i = 0; i < 4; ++i) {
+    r[i] = tile[(k0 + 4 * g + i) * stride + col];
+    r[4 + i] = tile[(k0 + 8 + 4 * g + i) * stride + col];
   }
+  return r;
+}
+
+// Row strides (elements) of LDS tiles, chosen against 4-byte bank conflicts:
+//   nat  -- tiles read only by lds_row8 (16 consecutive rows, 16 bytes each):
+//           16 bytes of padding, so the rows start 4 banks apart;
+//   col  -- tiles read only by lds_col8 (4 rows x 32 bytes per 16 lanes): bf16
+//           rows start 16 banks apart (64 bytes of padding);
+//   both -- tiles read both ways: bf16 rows start 12 banks apart.
+template <typename T, int D> struct Stride {
+  static constexpr int nat = D + 16 / (int)sizeof(T);
+  static constexpr int col = sizeof(T) == 2 ? D + 32 : D + 4;
+  static constexpr int both = sizeof(T) == 2 ? D + 24 : D + 4;
 };
 
 }  // namespace e3

@@ -112,7 +112,8 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const Args a) {
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
   const int BH = a.B * a.H;
-  const int kt = blockIdx.x / BH, bh = blockIdx.x % BH, b = bh / a.H, h = bh % a.H;
+  const int kt = tile_order(blockIdx.x / BH, (a.Tkv + BNK - 1) / BNK), bh = blockIdx.x % BH,
+            b = bh / a.H, h = bh % a.H;
   const Geo geo{a.layout, a.cp, a.rank, a.T, a.Tkv};
   const int kt0 = kt * BNK;
   const int kt1 = (kt0 + BNK) < a.Tkv ? (kt0 + BNK) : a.Tkv;
@@ -291,8 +292,12 @@ struct DqCfg {
   static constexpr int NB = 4;              // diagonal blocks per epilogue group
 };
 
+#ifndef E3_DQ_OCC
+#define E3_DQ_OCC 2
+#endif
+
 template <typename T, int D>
-__global__ __launch_bounds__(256, 2) void dq_kernel(const Args a) {
+__global__ __launch_bounds__(256, E3_DQ_OCC) void dq_kernel(const Args a) {
   using C = DqCfg<T, D>;
   using Op = typename V8<T>::type;
   constexpr int BM = C::BM, BN = C::BN, KS = C::KS, DB = C::DB;

@@ -49,6 +49,21 @@ struct Args {
   int layout, cp, rank;
 };
 
+// Launch order of tiles. 0: most work first. 1: alternate the heaviest and the
+// lightest remaining tile, so that co-resident workgroups mix MFMA-heavy main
+// loops with memory-heavy epilogues.
+#ifndef E3_TILE_ORDER
+#define E3_TILE_ORDER 0
+#endif
+__host__ __device__ inline int tile_order(int o, int n) {
+#if E3_TILE_ORDER == 1
+  return (o & 1) ? n - 1 - (o >> 1) : (o >> 1);
+#else
+  (void)n;
+  return o;
+#endif
+}
+
 // Measurement hook (host): records the next caller-provided timing event, if any,
 // on the stream. Called before the first kernel of an entry point and after each.
 void timing_mark(hipStream_t st);
@@ -118,7 +133,8 @@ struct Geo {
   // Query tile in launch order: the latest global positions (the most block-0
   // keys) first. Returns the local first row, the row count and the global
   // position of the first row.
-  __host__ __device__ void qtile(int trank, int BM, int& row0, int& nrows, int& gpos0) const {
+  __host__ __device__ void qtile(int order, int BM, int& row0, int& nrows, int& gpos0) const {
+    int trank = tile_order(order, ntiles(BM));
     for (int r = nruns() - 1; r >= 0; --r) {
       int ls, len, gb;
       run(r, ls, len, gb);

@@ -42,13 +42,29 @@ def oracle_cp(w):
 
 
 def run_oracle(w: synth.Workload, inp: dict, heads=None, rows=256):
-    f = {k: v.double().numpy() for k, v in inp.items()}
+    """Oracle forward + backward for the requested heads (all by default). Inputs
+    are converted to float64 one head at a time to bound host memory."""
+    hs = list(range(w.H)) if heads is None else list(heads)
+    B, T, N, D = w.B, w.T, w.N, w.D
     cu = w.cu_seqlens()
-    out, lse = oracle.forward(f["q"], f["k0"], f["v0"], f["kd"], f["vd"], w.scale, cu, w.layout,
-                              oracle_cp(w), w.rank, heads=heads, rows=rows)
-    grads = oracle.backward(f["dout"], f["q"], f["k0"], f["v0"], f["kd"], f["vd"], w.scale, cu,
-                            w.layout, oracle_cp(w), w.rank, out=out, lse=lse, heads=heads, rows=rows)
-    return out, lse, grads
+    qpos = oracle.query_positions(w.layout, T, oracle_cp(w), w.rank)
+    out = np.zeros((B, T, len(hs), D))
+    lse = np.zeros((B, len(hs), T))
+    dq = np.zeros((B, T, len(hs), D))
+    dk0 = np.zeros((B, w.T_kv, len(hs), D))
+    dv0 = np.zeros((B, w.T_kv, len(hs), D))
+    dkd = np.zeros((B, N, T, len(hs), D))
+    dvd = np.zeros((B, N, T, len(hs), D))
+    f = lambda t: t.double().numpy()
+    for b in range(B):
+        for j, h in enumerate(hs):
+            q, k0, v0 = f(inp["q"][b, :, h]), f(inp["k0"][b, :, h]), f(inp["v0"][b, :, h])
+            kd, vd, do = f(inp["kd"][b, :, :, h]), f(inp["vd"][b, :, :, h]), f(inp["dout"][b, :, h])
+            o, l = oracle.forward_head(q, k0, v0, kd, vd, w.scale, qpos, cu, rows)
+            g = oracle.backward_head(do, q, k0, v0, kd, vd, w.scale, qpos, cu, out=o, lse=l, rows=rows)
+            out[b, :, j], lse[b, j] = o, l
+            dq[b, :, j], dk0[b, :, j], dv0[b, :, j], dkd[b, :, :, j], dvd[b, :, :, j] = g
+    return out, lse, (dq, dk0, dv0, dkd, dvd)
 
 
 def rel(a, b):

@@ -28,7 +28,7 @@ if ROOT not in sys.path:
 METRIC = "EAGLE-3 mixed attn fwd+bwd TFLOP/s (causal) + % bf16 MFMA peak, T=4096 H=32 D=128"
 PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}   # MI355X dense MFMA (bf16) / fp32 vector
 PEAK_GBS = 8000.0                               # MI355X HBM3E
-KERNELS = ["fwd", "delta", "dkdv", "dq"]
+KERNELS = ["xpose_v", "fwd", "delta", "dkdv", "dq"]
 
 
 def log(msg):
@@ -46,6 +46,8 @@ def kernel_work(w, P0):
     pf = B * H * D * P0                       # one D-long dot per attended pair
     diagf = B * H * D * T * N
     return {
+        # v0 read, its transposed copy written
+        "xpose_v": dict(flop=0, diag_flop=0, bytes=2 * ukv),
         # q, k0, v0, kd, vd read; out, lse written
         "fwd": dict(flop=4 * pf, diag_flop=4 * diagf, bytes=u + 2 * ukv + 2 * N * u + u + rowf),
         # dO, O read; delta written
@@ -165,10 +167,11 @@ def main():
     grads = (torch.empty_like(d["q"]), torch.empty_like(d["k0"]), torch.empty_like(d["v0"]),
              torch.empty_like(d["kd"]), torch.empty_like(d["vd"]))
     ws = torch.empty(max(prob.workspace_bytes(), 256), dtype=torch.uint8, device=dev)
+    fws = torch.empty(max(prob.fwd_workspace_bytes(), 256), dtype=torch.uint8, device=dev)
     lib = e3.lib()
 
     def step():
-        e3.fwd(prob, d["q"], d["k0"], d["v0"], d["kd"], d["vd"], out=out, lse=lse)
+        e3.fwd(prob, d["q"], d["k0"], d["v0"], d["kd"], d["vd"], out=out, lse=lse, workspace=fws)
         e3.bwd(prob, d["dout"], d["q"], d["k0"], d["v0"], d["kd"], d["vd"], out, lse,
                grads=grads, workspace=ws)
 
@@ -194,7 +197,7 @@ def main():
     log(f"[bench] {args.steps} steps: {total_ms:.3f} ms ({ms_per_step:.4f} ms/step, wall {wall_ms:.1f} ms)")
 
     # (2) per-kernel times: events recorded by the library around each kernel
-    nfwd, nbwd = 2, 4
+    nfwd, nbwd = 3, 4
     per = {k: [] for k in KERNELS}
     fwd_ms, bwd_ms, flushed = [], [], []
     flush_buf = None if args.no_flush else torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -206,7 +209,7 @@ def main():
             flush_buf.zero_()     # evict L2 and MALL between steps (outside the events)
         psz = ctypes.sizeof(ctypes.c_void_p)
         lib.eagle3_set_timing_events(ctypes.c_void_p(ctypes.addressof(evf) + r * nfwd * psz), nfwd)
-        e3.fwd(prob, d["q"], d["k0"], d["v0"], d["kd"], d["vd"], out=out, lse=lse)
+        e3.fwd(prob, d["q"], d["k0"], d["v0"], d["kd"], d["vd"], out=out, lse=lse, workspace=fws)
         assert lib.eagle3_timing_events_recorded() == nfwd
         lib.eagle3_set_timing_events(ctypes.c_void_p(ctypes.addressof(evb) + r * nbwd * psz), nbwd)
         e3.bwd(prob, d["dout"], d["q"], d["k0"], d["v0"], d["kd"], d["vd"], out, lse,
@@ -217,11 +220,12 @@ def main():
     for r in range(reps):
         f0 = r * nfwd
         b0 = r * nbwd
-        per["fwd"].append(ev.elapsed_ms(evf[f0], evf[f0 + 1]))
+        per["xpose_v"].append(ev.elapsed_ms(evf[f0], evf[f0 + 1]))
+        per["fwd"].append(ev.elapsed_ms(evf[f0 + 1], evf[f0 + 2]))
         per["delta"].append(ev.elapsed_ms(evb[b0], evb[b0 + 1]))
         per["dkdv"].append(ev.elapsed_ms(evb[b0 + 1], evb[b0 + 2]))
         per["dq"].append(ev.elapsed_ms(evb[b0 + 2], evb[b0 + 3]))
-        fwd_ms.append(per["fwd"][-1])
+        fwd_ms.append(ev.elapsed_ms(evf[f0], evf[f0 + 2]))
         bwd_ms.append(ev.elapsed_ms(evb[b0], evb[b0 + 3]))
         flushed.append(fwd_ms[-1] + bwd_ms[-1])
     ev.destroy(se)

@@ -122,6 +122,8 @@ int validate(const e3_problem* p, Resolved& r, bool whole, bool need_dev = true)
   return E3_OK;
 }
 
+e3::Geo geo_of(const e3_problem* p) { return e3::Geo{p->layout, p->cp, p->rank, p->T, p->T_kv}; }
+
 e3::Args make_args(const e3_problem* p, const Resolved& r) {
   e3::Args a{};
   a.cu = p->num_docs > 1 ? p->cu_seqlens_dev : nullptr;
@@ -151,15 +153,15 @@ int check_ptrs(const char* const* names, const void* const* ptrs, int n) {
 }
 
 int fwd_impl(const e3_problem* p, const void* q, const void* k0, const void* v0, const void* kd,
-             const void* vd, void* out, float* lse, hipStream_t st, bool whole) {
+             const void* vd, void* out, float* lse, void* ws, hipStream_t st, bool whole) {
   Resolved r;
   int rc = validate(p, r, whole);
   if (rc) return rc;
   if (p->T == 0) return ok();
   {
-    const char* names[] = {"q", "k0", "v0", "out", "lse"};
-    const void* ptrs[] = {q, k0, v0, out, lse};
-    if ((rc = check_ptrs(names, ptrs, 5))) return rc;
+    const char* names[] = {"q", "k0", "v0", "out", "lse", "workspace"};
+    const void* ptrs[] = {q, k0, v0, out, lse, ws};
+    if ((rc = check_ptrs(names, ptrs, 6))) return rc;
   }
   if (r.N > 0) {
     const char* names[] = {"kd", "vd"};
@@ -175,6 +177,8 @@ int fwd_impl(const e3_problem* p, const void* q, const void* k0, const void* v0,
   a.vd = vd;
   a.out = out;
   a.lse = lse;
+  a.vt = ws;
+  a.kv_pitch = geo_of(p).kvruns().pitch;
   hipError_t e = e3::launch_fwd(a, p->dtype, p->D, st);
   if (e != hipSuccess) return fail(E3_EHIP, "forward launch failed: %s", hipGetErrorString(e));
   return ok();
@@ -218,8 +222,6 @@ int bwd_impl(const e3_problem* p, const void* dout, const void* q, const void* k
   return ok();
 }
 
-e3::Geo geo_of(const e3_problem* p) { return e3::Geo{p->layout, p->cp, p->rank, p->T, p->T_kv}; }
-
 int doc_lo_host(const e3_problem* p, int pos) {
   return e3::doc_lo_of(p->cu_seqlens_host, p->num_docs > 1 ? p->num_docs : 1, pos);
 }
@@ -253,14 +255,25 @@ size_t eagle3_bwd_workspace_bytes(const e3_problem* p) {
   return (n + 255) & ~(size_t)255;
 }
 
+size_t eagle3_fwd_workspace_bytes(const e3_problem* p) {
+  Resolved r;
+  if (validate(p, r, false, false)) return 0;
+  g_err.clear();
+  if (p->T == 0) return 0;
+  const size_t esz = p->dtype == E3_BF16 ? 2 : 4;
+  const size_t n = (size_t)p->B * p->H * p->D * geo_of(p).kvruns().pitch * esz;
+  return (n + 255) & ~(size_t)255;
+}
+
 int eagle3_attn_fwd(const e3_problem* p, const void* q, const void* k0, const void* v0, const void* kd,
-                    const void* vd, void* out, float* lse, hipStream_t stream) {
-  return fwd_impl(p, q, k0, v0, kd, vd, out, lse, stream, true);
+                    const void* vd, void* out, float* lse, void* workspace, hipStream_t stream) {
+  return fwd_impl(p, q, k0, v0, kd, vd, out, lse, workspace, stream, true);
 }
 
 int eagle3_shard_fwd(const e3_problem* p, const void* q, const void* k0, const void* v0,
-                     const void* kd, const void* vd, void* out, float* lse, hipStream_t stream) {
-  return fwd_impl(p, q, k0, v0, kd, vd, out, lse, stream, false);
+                     const void* kd, const void* vd, void* out, float* lse, void* workspace,
+                     hipStream_t stream) {
+  return fwd_impl(p, q, k0, v0, kd, vd, out, lse, workspace, stream, false);
 }
 
 int eagle3_attn_bwd(const e3_problem* p, const void* dout, const void* q, const void* k0,
@@ -357,7 +370,7 @@ int eagle3_fwd_tile_segments(const e3_problem* p, int tile, int32_t* rows, int32
     if (seg && n < max_segments) {
       const int s0 = it.s0, e = (s0 + BN) < it.b ? (s0 + BN) : it.b;
       const bool interior = s0 >= it.a && s0 + BN <= it.b && s0 >= lo_max && s0 + BN - 1 <= g_min;
-      seg[3 * n + 0] = s0;
+      seg[3 * n + 0] = s0 > it.a ? s0 : it.a;
       seg[3 * n + 1] = e;
       seg[3 * n + 2] = interior ? 0 : 1;
     }

@@ -183,6 +183,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const Args a) {
   QIter nx = it;
   if (nx.valid) nx.next(geo, BMQ);
   if (nx.valid) fetch(nx);
+  wait_all();
   __syncthreads();
 
   while (it.valid) {
@@ -289,7 +290,7 @@ struct DqCfg {
   static constexpr int LDS_KV = 2 * STAGE;
   static constexpr int LDS_EPI = 4 * 32 * OSTR * 4;
   static constexpr int LDS = LDS_KV > LDS_EPI ? LDS_KV : LDS_EPI;
-  static constexpr int NB = 4;              // diagonal blocks per epilogue group
+  static constexpr int NB = sizeof(T) == 2 ? 8 : 2;   // diagonal blocks per epilogue group
 };
 
 #ifndef E3_DQ_OCC
@@ -366,6 +367,7 @@ __global__ __launch_bounds__(256, E3_DQ_OCC) void dq_kernel(const Args a) {
   SegIter nx = it;
   if (nx.valid) nx.next(geo, BN);
   if (nx.valid) fetch(nx.s0);
+  wait_all();
   __syncthreads();
 
   while (it.valid) {
@@ -435,9 +437,11 @@ __global__ __launch_bounds__(256, E3_DQ_OCC) void dq_kernel(const Args a) {
     }
   __syncthreads();
 
+  // All kd/vd loads of a group of NB blocks are issued before any is used.
   constexpr int LPR = D / 8;
   constexpr int RPP = 64 / LPR;
   constexpr int NB = C::NB;
+  using V = typename V8<T>::type;
   const int lr = lane / LPR, cc = (lane % LPR) * 8;
   const T* kdb = reinterpret_cast<const T*>(a.kd) + (long long)b * a.kd_bs + (long long)h * D + cc;
   const T* vdb = reinterpret_cast<const T*>(a.vd) + (long long)b * a.kd_bs + (long long)h * D + cc;
@@ -451,46 +455,41 @@ __global__ __launch_bounds__(256, E3_DQ_OCC) void dq_kernel(const Args a) {
     const bool ok = tr < nrows;              // whole row groups agree
     const long long row = row0 + (ok ? tr : 0);
     f32x8 dqv = *reinterpret_cast<const f32x8*>(Qw + rr * C::OSTR + cc);
-    const f32x8 qv = load8f(qb + row * rs + cc);
-    const f32x8 ov = load8f(dob + row * rs + cc);
+    const V qv = load8(qb + row * rs + cc);
+    const V ov = load8(dob + row * rs + cc);
     const float l2 = lseb[row] * kLog2e;
     const float dl = delb[row];
     for (int i0 = 0; i0 < a.N; i0 += NB) {
       const int n = (a.N - i0) < NB ? (a.N - i0) : NB;
-      typename V8<T>::type kv[NB], vv[NB];
+      // Unconditional loads (block index clamped): conditional ones would be
+      // waited for one at a time.
+      V kv[NB], vv[NB];
 #pragma unroll
-      for (int i = 0; i < NB; ++i)
-        if (i < n) {
+      for (int i = 0; i < NB; ++i) {
+        const long long off = (long long)(i0 + (i < n ? i : n - 1)) * a.kd_blk + row * rs;
+        kv[i] = load8(kdb + off);
+        vv[i] = load8(vdb + off);
+      }
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        const float y = group_sum<LPR>(dot8(qv, kv[i], 0.f));
+        const float dpi = group_sum<LPR>(dot8(ov, vv[i], 0.f));
+        const float pi = i < n ? fast_exp2(y * c2 - l2) : 0.f;
+        const float ds = pi * (dpi - dl);
+        const float sds = scale * ds;
+        f32x8 gk, gv;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          dqv[e] = fmaf(ds, (float)kv[i][e], dqv[e]);
+          gk[e] = sds * (float)qv[e];
+          gv[e] = pi * (float)ov[e];
+        }
+        if (ok && i < n) {
           const long long off = (long long)(i0 + i) * a.kd_blk + row * rs;
-          kv[i] = load8(kdb + off);
-          vv[i] = load8(vdb + off);
+          store8f(dkdb + off, gk);
+          store8f(dvdb + off, gv);
         }
-#pragma unroll
-      for (int i = 0; i < NB; ++i)
-        if (i < n) {
-          float y = 0.f, dpi = 0.f;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            y += qv[e] * (float)kv[i][e];
-            dpi += ov[e] * (float)vv[i][e];
-          }
-          y = group_sum<LPR>(y);
-          dpi = group_sum<LPR>(dpi);
-          const float pi = fast_exp2(y * c2 - l2);
-          const float ds = pi * (dpi - dl);
-          f32x8 gk, gv;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            dqv[e] += ds * (float)kv[i][e];
-            gk[e] = scale * ds * qv[e];
-            gv[e] = pi * ov[e];
-          }
-          if (ok) {
-            const long long off = (long long)(i0 + i) * a.kd_blk + row * rs;
-            store8f(dkdb + off, gk);
-            store8f(dvdb + off, gv);
-          }
-        }
+      }
     }
     if (ok) {
 #pragma unroll

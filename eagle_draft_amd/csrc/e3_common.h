@@ -40,6 +40,12 @@ struct Args {
   void* dv0;
   void* dkd;
   void* dvd;
+  const void* vt;       // V^T of block 0 (transposed copy, see e3_xpose.hip)
+  const void* kt;       // K^T of block 0
+  const void* qt;       // Q^T of the local rows
+  const void* dot;      // dO^T of the local rows
+  int kv_pitch;         // positions per (b, h, d) row of kt / vt
+  int q_pitch;          // positions per (b, h, d) row of qt / dot
   const int32_t* cu;    // device cu_seqlens (global document boundaries)
   int ndocs;            // <= 1: one document
   int B, T, Tkv, H, N;
@@ -47,6 +53,14 @@ struct Args {
   float scale;
   float c2;             // scale * log2(e): scores are kept in the base-2 domain
   int layout, cp, rank;
+};
+
+// Row runs of a transposed copy: run i holds rows [src[i], src[i]+len[i]) of the
+// source at positions [dst[i], dst[i]+len[i]) of each (b, h, d) row of length pitch.
+struct XRuns {
+  int n;
+  int src[2], len[2], dst[2];
+  int pitch;
 };
 
 // Launch order of tiles. 0: most work first. 1: alternate the heaviest and the
@@ -67,6 +81,10 @@ __host__ __device__ inline int tile_order(int o, int n) {
 // Measurement hook (host): records the next caller-provided timing event, if any,
 // on the stream. Called before the first kernel of an entry point and after each.
 void timing_mark(hipStream_t st);
+
+// Writes the transposed copy of x [B, rows, H, D] (batch stride x_bs) laid out by runs.
+hipError_t launch_xpose(const void* x, long long x_bs, void* xt, const XRuns& runs, int B, int H,
+                        int dtype, int D, hipStream_t st);
 
 // ---------------------------------------------------------------------------
 // Share geometry (host and device)
@@ -119,6 +137,33 @@ struct Geo {
     }
   }
 
+  // Transposed-copy layout of the local query rows (one entry per run) and of
+  // the block-0 keys (one run).
+  __host__ __device__ XRuns qruns() const {
+    XRuns r{};
+    r.n = nruns();
+    int p = 0;
+    for (int i = 0; i < r.n; ++i) {
+      int ls, len, gb;
+      run(i, ls, len, gb);
+      r.src[i] = ls;
+      r.len[i] = len;
+      r.dst[i] = p;
+      p += (len + 63) / 64 * 64;
+    }
+    r.pitch = p;
+    return r;
+  }
+  __host__ __device__ XRuns kvruns() const {
+    XRuns r{};
+    r.n = 1;
+    r.src[0] = 0;
+    r.len[0] = Tkv;
+    r.dst[0] = 0;
+    r.pitch = (Tkv + 63) / 64 * 64;
+    return r;
+  }
+
   // Number of query tiles of height BM over all runs.
   __host__ __device__ int ntiles(int BM) const {
     int n = 0;
@@ -156,8 +201,9 @@ struct Geo {
 
 // Walks the block-0 key tiles of width BN that a query tile can see: segment by
 // segment in ring order, each segment clipped to the key window [wlo, whi).
-// Tile starts are aligned to BN relative to the segment start; keys of a tile
-// outside [a, b) or outside a row's visible range are masked by the kernel.
+// Tile starts are multiples of BN (so transposed copies are read aligned); keys
+// of a tile outside [a, b) or outside a row's visible range are masked by the
+// kernel.
 struct SegIter {
   int step, part, a, b, s0, end, wlo, whi;
   bool valid;
@@ -172,7 +218,7 @@ struct SegIter {
       const int lo = a > wlo ? a : wlo;
       const int hi = b < whi ? b : whi;
       if (lo < hi) {
-        s0 = a + ((lo - a) / BN) * BN;
+        s0 = (lo / BN) * BN;
         end = hi;
         valid = true;
         return;
@@ -237,6 +283,28 @@ __device__ __forceinline__ void mfma16(const bf16x8& a, const bf16x8& b, f32x16&
 __device__ __forceinline__ void mfma16(const f32x8& a, const f32x8& b, f32x16& c) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[i], c, 0, 0, 0);
+}
+
+// Waits for every outstanding memory operation of the wave. Placed before a
+// main loop so the loop header starts with nothing pending from the prologue;
+// otherwise the wait-count pass may merge the prologue's register loads into the
+// loop and wait for the next tile's prefetch at the top of every iteration.
+__device__ __forceinline__ void wait_all() { __builtin_amdgcn_s_waitcnt(0); }
+
+// <a, b> + acc over 8 elements: four packed bf16 dot products (v_dot2_f32_bf16)
+// or eight fp32 FMAs.
+__device__ __forceinline__ float dot8(const bf16x8& a, const bf16x8& b, float acc) {
+  typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(a, a, 0, 1), __builtin_shufflevector(b, b, 0, 1), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(a, a, 2, 3), __builtin_shufflevector(b, b, 2, 3), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(a, a, 4, 5), __builtin_shufflevector(b, b, 4, 5), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(a, a, 6, 7), __builtin_shufflevector(b, b, 6, 7), acc, false);
+  return acc;
+}
+__device__ __forceinline__ float dot8(const f32x8& a, const f32x8& b, float acc) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc = fmaf(a[e], b[e], acc);
+  return acc;
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

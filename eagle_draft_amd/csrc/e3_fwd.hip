@@ -23,16 +23,16 @@ struct FwdCfg {
   static constexpr int NT = 256;
   static constexpr int BM = 128;
   static constexpr int BN = 64;
-  static constexpr int KSTR = Stride<T, D>::nat;
-  static constexpr int VSTR = Stride<T, D>::col;
+  static constexpr int KSTR = Stride<T, D>::nat;        // K tile [BN keys][D]
+  static constexpr int VSTR = Stride<T, BN>::nat;       // V^T tile [D][BN keys]
   static constexpr int OSTR = D + 4;       // fp32 staging rows of the epilogue
   static constexpr int KS = D / 16;        // MFMA k-steps over D
   static constexpr int DB = D / 32;        // 32-row blocks of O^T
-  static constexpr int STAGE = (BN * KSTR + BN * VSTR) * (int)sizeof(T);
+  static constexpr int STAGE = (BN * KSTR + D * VSTR) * (int)sizeof(T);
   static constexpr int LDS_KV = 2 * STAGE;
   static constexpr int LDS_EPI = 4 * 32 * OSTR * 4 + 2 * BM * 4;
   static constexpr int LDS = LDS_KV > LDS_EPI ? LDS_KV : LDS_EPI;
-  static constexpr int NB = sizeof(T) == 2 ? 8 : 4;   // diagonal blocks per epilogue group
+  static constexpr int NB = sizeof(T) == 2 ? 8 : 2;   // diagonal blocks per epilogue group
 };
 
 constexpr float kRescaleSlack = 8.0f;      // log2 of the largest un-rescaled growth
@@ -54,7 +54,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const Args a) {
   const long long rs = (long long)a.H * D;
   const T* qb = reinterpret_cast<const T*>(a.q) + (long long)b * a.T * rs + (long long)h * D;
   const T* k0b = reinterpret_cast<const T*>(a.k0) + (long long)b * a.k0_bs + (long long)h * D;
-  const T* v0b = reinterpret_cast<const T*>(a.v0) + (long long)b * a.k0_bs + (long long)h * D;
+  const T* vtb = reinterpret_cast<const T*>(a.vt) + ((long long)b * a.H + h) * D * a.kv_pitch;
 
   // This lane's query row.
   const int qr = w * 32 + l32;
@@ -80,20 +80,17 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const Args a) {
   const float c2 = a.c2;
 
   auto kbuf = [&](int s) { return reinterpret_cast<T*>(smem + s * C::STAGE); };
-  auto vbuf = [&](int s) { return reinterpret_cast<T*>(smem + s * C::STAGE) + BN * C::KSTR; };
+  auto vbuf = [&](int s) { return reinterpret_cast<T*>(smem + s * C::STAGE) + BN * C::KSTR; };  // V^T
 
   SegIter it;
   it.begin(geo, lo_min, g_max + 1, BN);
-  TileLoad<T, BN, D, 256> kt, vt;
+  TileLoad<T, BN, D, 256> kt;
+  TileLoad<T, D, BN, 256> vt;   // V^T: D rows of BN key positions (zero padded)
   auto fetch = [&](int s0) {
     const int nv = a.Tkv - s0;
-    if (nv >= BN) {
-      kt.load_full(k0b + (long long)s0 * rs, rs, tid);
-      vt.load_full(v0b + (long long)s0 * rs, rs, tid);
-    } else {
-      kt.load(k0b + (long long)s0 * rs, rs, nv, tid);
-      vt.load(v0b + (long long)s0 * rs, rs, nv, tid);
-    }
+    if (nv >= BN) kt.load_full(k0b + (long long)s0 * rs, rs, tid);
+    else kt.load(k0b + (long long)s0 * rs, rs, nv, tid);
+    vt.load_full(vtb + s0, a.kv_pitch, tid);
   };
   // Prologue: tile 0 into stage 0, tile 1 into registers.
   int stage = 0;
@@ -105,6 +102,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const Args a) {
   SegIter nx = it;
   if (nx.valid) nx.next(geo, BN);
   if (nx.valid) fetch(nx.s0);
+  wait_all();
   __syncthreads();
 
   while (it.valid) {
@@ -113,14 +111,27 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const Args a) {
     const T* Vs = vbuf(stage);
 
     // S^T for keys [s0, s0+64): two 32-key blocks, lane = query, 16 keys per block.
+    // The two accumulator chains alternate and operands are read a step ahead.
     f32x16 st[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int j = 0; j < 16; ++j) st[kb][j] = 0.f;
+    {
+      Op a0 = lds_row8(Ks, C::KSTR, l32, 8 * g);
+      Op a1 = lds_row8(Ks, C::KSTR, 32 + l32, 8 * g);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        mfma16(lds_row8(Ks, C::KSTR, 32 * kb + l32, 16 * ks + 8 * g), qreg[ks], st[kb]);
+      for (int ks = 0; ks < KS; ++ks) {
+        Op n0 = a0, n1 = a1;
+        if (ks + 1 < KS) {
+          n0 = lds_row8(Ks, C::KSTR, l32, 16 * (ks + 1) + 8 * g);
+          n1 = lds_row8(Ks, C::KSTR, 32 + l32, 16 * (ks + 1) + 8 * g);
+        }
+        mfma16(a0, qreg[ks], st[0]);
+        mfma16(a1, qreg[ks], st[1]);
+        a0 = n0;
+        a1 = n1;
+      }
     }
     const bool interior = s0 >= sa && s0 + BN <= sb && s0 >= lo_max && s0 + BN - 1 <= g_min;
     float mx = kNegInf;
@@ -163,12 +174,22 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const Args a) {
       }
     l_i += rsum;
     // O^T += V^T P^T over the 64 keys (4 k-steps of 16).
+    {
+      Op pv[BN / 16];
 #pragma unroll
-    for (int ks = 0; ks < BN / 16; ++ks) {
-      const Op pv = to_op(st[ks >> 1], 8 * (ks & 1), T());
+      for (int ks = 0; ks < BN / 16; ++ks) pv[ks] = to_op(st[ks >> 1], 8 * (ks & 1), T());
+      Op va[DB];
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
-        mfma16(lds_col8(Vs, C::VSTR, 16 * ks, 32 * db, lane), pv, acc[db]);
+      for (int db = 0; db < DB; ++db) va[db] = lds_row8(Vs, C::VSTR, 32 * db + l32, 8 * g);
+#pragma unroll
+      for (int ks = 0; ks < BN / 16; ++ks) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const Op cur = va[db];
+          if (ks + 1 < BN / 16) va[db] = lds_row8(Vs, C::VSTR, 32 * db + l32, 16 * (ks + 1) + 8 * g);
+          mfma16(cur, pv[ks], acc[db]);
+        }
+      }
     }
 
     // Next tile: registers -> the other stage; fetch the one after.
@@ -206,64 +227,79 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const Args a) {
   __syncthreads();
 
   // ---- diagonal blocks, row-major: LPR lanes per row, 8 columns per lane ----
-  // All kd/vd loads of a group of NB blocks are issued before any is used.
+  // Two row passes at a time, and all kd/vd loads of a group of NB blocks for
+  // both issued before any is used (the epilogue is bound by memory latency).
   constexpr int LPR = D / 8;
   constexpr int RPP = 64 / LPR;
   constexpr int NB = C::NB;
+  using V = typename V8<T>::type;
   const int lr = lane / LPR, cc = (lane % LPR) * 8;
   const T* kdb = reinterpret_cast<const T*>(a.kd) + (long long)b * a.kd_bs + (long long)h * D + cc;
   const T* vdb = reinterpret_cast<const T*>(a.vd) + (long long)b * a.kd_bs + (long long)h * D + cc;
   T* ob = reinterpret_cast<T*>(a.out) + (long long)b * a.T * rs + (long long)h * D + cc;
   float* lseb = a.lse + ((long long)b * a.H + h) * a.T;
-  for (int pass = 0; pass < 32 / RPP; ++pass) {
-    const int rr = pass * RPP + lr;
-    const int tr = w * 32 + rr;
-    const bool ok = tr < nrows;                // whole row groups agree
-    const long long row = row0 + (ok ? tr : 0);
-    float m = Ms[tr], l = Ls[tr];
-    f32x8 o = *reinterpret_cast<const f32x8*>(Ow + rr * C::OSTR + cc);
-    const f32x8 qv = load8f(qb + row * rs + cc);
+  for (int pass = 0; pass < 32 / RPP; pass += 2) {
+    bool ok[2];
+    long long row[2];
+    float m[2], l[2];
+    f32x8 o[2];
+    V qv[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int rr = (pass + u) * RPP + lr;
+      const int tr = w * 32 + rr;
+      ok[u] = tr < nrows;                      // whole row groups agree
+      row[u] = row0 + (ok[u] ? tr : 0);
+      m[u] = Ms[tr];
+      l[u] = Ls[tr];
+      o[u] = *reinterpret_cast<const f32x8*>(Ow + rr * C::OSTR + cc);
+      qv[u] = load8(qb + row[u] * rs + cc);
+    }
     for (int i0 = 0; i0 < a.N; i0 += NB) {
       const int n = (a.N - i0) < NB ? (a.N - i0) : NB;
-      typename V8<T>::type kv[NB], vv[NB];
+      // Unconditional loads (block index clamped): conditional ones would be
+      // waited for one at a time.
+      V kv[2][NB], vv[2][NB];
 #pragma unroll
       for (int i = 0; i < NB; ++i)
-        if (i < n) {
-          const long long off = (long long)(i0 + i) * a.kd_blk + row * rs;
-          kv[i] = load8(kdb + off);
-          vv[i] = load8(vdb + off);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const long long off = (long long)(i0 + (i < n ? i : n - 1)) * a.kd_blk + row[u] * rs;
+          kv[u][i] = load8(kdb + off);
+          vv[u][i] = load8(vdb + off);
         }
-      float y[NB];
-      float mg = m;
 #pragma unroll
-      for (int i = 0; i < NB; ++i)
-        if (i < n) {
-          float d = 0.f;
+      for (int u = 0; u < 2; ++u) {
+        float y[NB];
+        float mg = m[u];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) d += qv[e] * (float)kv[i][e];
-          y[i] = group_sum<LPR>(d) * c2;
+        for (int i = 0; i < NB; ++i) {
+          const float d = group_sum<LPR>(dot8(qv[u], kv[u][i], 0.f));
+          y[i] = i < n ? d * c2 : kNegInf;
           mg = fmaxf(mg, y[i]);
         }
-      const float al = fast_exp2(m - mg);
-      l *= al;
+        const float al = fast_exp2(m[u] - mg);
+        l[u] *= al;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] *= al;
+        for (int e = 0; e < 8; ++e) o[u][e] *= al;
 #pragma unroll
-      for (int i = 0; i < NB; ++i)
-        if (i < n) {
+        for (int i = 0; i < NB; ++i) {
           const float p = fast_exp2(y[i] - mg);
-          l += p;
+          l[u] += p;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) o[e] += p * (float)vv[i][e];
+          for (int e = 0; e < 8; ++e) o[u][e] = fmaf(p, (float)vv[u][i][e], o[u][e]);
         }
-      m = mg;
+        m[u] = mg;
+      }
     }
-    if (ok) {
-      const float inv = 1.f / l;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] *= inv;
-      store8f(ob + row * rs, o);
-      if ((lane % LPR) == 0) lseb[row] = (m + fast_log2(l)) * kLn2;
+    for (int u = 0; u < 2; ++u) {
+      if (!ok[u]) continue;
+      const float inv = 1.f / l[u];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[u][e] *= inv;
+      store8f(ob + row[u] * rs, o[u]);
+      if ((lane % LPR) == 0) lseb[row[u]] = (m[u] + fast_log2(l[u])) * kLn2;
     }
   }
 }
@@ -273,6 +309,10 @@ static hipError_t launch_fwd_t(const Args& a, hipStream_t st) {
   const Geo geo{a.layout, a.cp, a.rank, a.T, a.Tkv};
   const long long nt = (long long)geo.ntiles(FwdCfg<T, D>::BM) * a.B * a.H;
   if (nt == 0) return hipSuccess;
+  timing_mark(st);
+  hipError_t e = launch_xpose(a.v0, a.k0_bs, const_cast<void*>(a.vt), geo.kvruns(), a.B, a.H,
+                              sizeof(T) == 2 ? 0 : 1, D, st);
+  if (e != hipSuccess) return e;
   timing_mark(st);
   hipLaunchKernelGGL((fwd_kernel<T, D>), dim3((unsigned)nt), dim3(256), 0, st, a);
   timing_mark(st);

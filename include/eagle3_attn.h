@@ -71,7 +71,7 @@
 extern "C" {
 #endif
 
-#define EAGLE3_ABI_VERSION 1
+#define EAGLE3_ABI_VERSION 2
 
 typedef enum { E3_OK = 0, E3_EINVAL = -1, E3_EUNSUPPORTED = -2, E3_EHIP = -3 } e3_status;
 typedef enum { E3_BF16 = 0, E3_F32 = 1 } e3_dtype;
@@ -115,11 +115,17 @@ const char* eagle3_last_error(void);
  * problem. */
 size_t eagle3_bwd_workspace_bytes(const e3_problem* p);
 
+/* Bytes of device workspace the forward needs: a transposed copy of v0 (dtype
+ * [B, H, D, P], P = T_kv rounded up to 64). 0 when T == 0. */
+size_t eagle3_fwd_workspace_bytes(const e3_problem* p);
+
 /* Forward of the full sequence (layout FULL or HEADSHARD):
  *   out [B,T,H,D] (dtype) = the joint-softmax output, lse [B,H,T] float32 = the merged
- *   log-sum-exp. kd/vd may be NULL when num_blocks == 1. */
+ *   log-sum-exp. kd/vd may be NULL when num_blocks == 1. workspace must hold
+ *   eagle3_fwd_workspace_bytes(p) bytes, 256-byte aligned; its contents are scratch. */
 int eagle3_attn_fwd(const e3_problem* p, const void* q, const void* k0, const void* v0,
-                    const void* kd, const void* vd, void* out, float* lse, hipStream_t stream);
+                    const void* kd, const void* vd, void* out, float* lse, void* workspace,
+                    hipStream_t stream);
 
 /* Backward of the full sequence (layout FULL or HEADSHARD) against the MERGED out/lse
  * produced by the forward: writes dq [B,T,H,D], dk0/dv0 [B,T_kv,H,D], dkd/dvd
@@ -135,7 +141,8 @@ int eagle3_attn_bwd(const e3_problem* p, const void* dout, const void* q, const 
  * them with the diagonals in one pass, with no inter-GPU communication. Arguments as
  * eagle3_attn_fwd / eagle3_attn_bwd. */
 int eagle3_shard_fwd(const e3_problem* p, const void* q, const void* k0, const void* v0,
-                     const void* kd, const void* vd, void* out, float* lse, hipStream_t stream);
+                     const void* kd, const void* vd, void* out, float* lse, void* workspace,
+                     hipStream_t stream);
 int eagle3_shard_bwd(const e3_problem* p, const void* dout, const void* q, const void* k0,
                      const void* v0, const void* kd, const void* vd, const void* out,
                      const float* lse, void* workspace, void* dq, void* dk0, void* dv0,
@@ -161,8 +168,9 @@ int lse_merge(float* out, float* lse, const float* block_out, const float* block
 
 /* While `events` is non-NULL, every compute entry point called on this thread records
  * events[0] on its stream before its first kernel and events[k+1] after its k-th kernel
- * (at most `capacity` events; the forward launches 1 kernel, the backward 3: delta, dK/dV,
- * dQ). The caller creates and owns the events; NULL stops recording. Returns E3_OK. */
+ * (at most `capacity` events; the forward launches 2 kernels: the V transpose and the
+ * attention kernel; the backward 3: delta, dK/dV, dQ). The caller creates and owns the
+ * events; NULL stops recording. Returns E3_OK. */
 int eagle3_set_timing_events(hipEvent_t* events, int capacity);
 
 /* Number of events recorded by the last compute entry point called on this thread. */
@@ -180,9 +188,10 @@ int64_t eagle3_pair_count(const e3_problem* p);
 int eagle3_fwd_tiles(const e3_problem* p, int32_t* tile_rows);
 
 /* Query tile `tile` (0-based, launch order) of the forward: writes its local row range
- * to rows_host[2] = {first, end} and its block-0 key segments, in the order the kernel
- * visits them, to seg_host[3*k] = {key_begin, key_end, needs_mask} for k < max_segments.
- * Returns the number of segments (may exceed max_segments) or a negative e3_status. */
+ * to rows_host[2] = {first, end} and the block-0 keys each key tile it visits may count,
+ * in visiting order, to seg_host[3*k] = {key_begin, key_end, needs_mask} for
+ * k < max_segments (the tile's keys clipped to its ring segment). Returns the number of
+ * key tiles (may exceed max_segments) or a negative e3_status. */
 int eagle3_fwd_tile_segments(const e3_problem* p, int tile, int32_t* rows_host,
                              int32_t* seg_host, int max_segments);
 

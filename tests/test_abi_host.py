@@ -63,27 +63,30 @@ def test_invalid_problems_are_rejected_before_launch(kw, code, msg):
     p = prob(**kw)
     lib = e3.lib()
     fake = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
-    rc = lib.eagle3_shard_fwd(p.ref(), fake, fake, fake, fake, fake, fake, fake, None)
+    rc = lib.eagle3_shard_fwd(p.ref(), fake, fake, fake, fake, fake, fake, fake, fake, None)
     assert rc == code
     assert msg in lib.eagle3_last_error().decode()
     rc = lib.eagle3_shard_bwd(p.ref(), *([fake] * 14), None)
     assert rc == code
     assert lib.eagle3_bwd_workspace_bytes(p.ref()) == 0
+    assert lib.eagle3_fwd_workspace_bytes(p.ref()) == 0
 
 
 def test_null_and_misaligned_pointers_are_rejected():
     lib = e3.lib()
     p = prob()
     a = ctypes.c_void_p(0x1000)
-    rc = lib.eagle3_attn_fwd(p.ref(), None, a, a, a, a, a, a, None)
+    rc = lib.eagle3_attn_fwd(p.ref(), None, a, a, a, a, a, a, a, None)
     assert rc == e3.E3_EINVAL and "q is NULL" in lib.eagle3_last_error().decode()
-    rc = lib.eagle3_attn_fwd(p.ref(), a, a, a, ctypes.c_void_p(0x1008), a, a, a, None)
+    rc = lib.eagle3_attn_fwd(p.ref(), a, a, a, a, a, a, a, None, None)
+    assert rc == e3.E3_EINVAL and "workspace is NULL" in lib.eagle3_last_error().decode()
+    rc = lib.eagle3_attn_fwd(p.ref(), a, a, a, ctypes.c_void_p(0x1008), a, a, a, a, None)
     assert rc == e3.E3_EINVAL and "kd is not 16-byte aligned" in lib.eagle3_last_error().decode()
     rc = lib.eagle3_attn_bwd(p.ref(), *([a] * 13), None, None)
     assert rc == e3.E3_EINVAL and "dvd is NULL" in lib.eagle3_last_error().decode()
     # the full-sequence entry points refuse a ring share
     q = prob(layout="zigzag", cp=2, T=256, T_kv=512)
-    rc = lib.eagle3_attn_fwd(q.ref(), *([a] * 7), None)
+    rc = lib.eagle3_attn_fwd(q.ref(), *([a] * 8), None)
     assert rc == e3.E3_EINVAL and "eagle3_shard_fwd" in lib.eagle3_last_error().decode()
     # lse_merge shape checks
     rc = lib.lse_merge(a, a, a, a, 1, 4, 2, 6, 0, None)
@@ -92,7 +95,7 @@ def test_null_and_misaligned_pointers_are_rejected():
     assert rc == e3.E3_EINVAL
     # an empty problem is a valid no-op
     z = prob(T=0, T_kv=0)
-    assert lib.eagle3_attn_fwd(z.ref(), *([None] * 7), None) == e3.E3_OK
+    assert lib.eagle3_attn_fwd(z.ref(), *([None] * 8), None) == e3.E3_OK
     assert lib.eagle3_attn_bwd(z.ref(), *([None] * 14), None) == e3.E3_OK
     assert lib.lse_merge(None, None, None, None, 1, 0, 2, 8, 0, None) == e3.E3_OK
 
@@ -100,6 +103,8 @@ def test_null_and_misaligned_pointers_are_rejected():
 def test_workspace_bytes():
     p = prob(B=1, T=1000, T_kv=1000, H=3)
     assert p.workspace_bytes() == ((1 * 3 * 1000 * 4 + 255) // 256) * 256
+    # transposed v0: [B, H, D, T_kv rounded up to 64], bf16
+    assert p.fwd_workspace_bytes() == ((1 * 3 * 128 * 1024 * 2 + 255) // 256) * 256
 
 
 SHARES = [

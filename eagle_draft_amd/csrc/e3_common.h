@@ -327,6 +327,34 @@ __device__ __forceinline__ float xor32(float x) {
   return __shfl_xor(x, 32);
 }
 
+// An empty asm that takes and returns `x` in registers: the value has to be
+// computed before this point and stays ordered with the other volatile asm and
+// scheduling fences around it (it cannot be sunk into later blocks).
+template <typename V>
+__device__ __forceinline__ void pin(V& x) {
+  asm volatile("" : "+v"(x));
+}
+
+// max / sum of the values of lanes l and l^32, in every lane: one
+// v_permlane32_swap (VALU; no LDS round trip) and one combining op. The two
+// halves add in the same order, so both get bit-identical sums.
+__device__ __forceinline__ void swap32(float x, float& lo, float& hi) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const unsigned a = r[0], b = r[1];     // copy out: bit-casting a vector element misreads it
+  lo = __uint_as_float(a);               // value of lane l & 31
+  hi = __uint_as_float(b);               // value of lane (l & 31) + 32
+}
+__device__ __forceinline__ float swap32_max(float x) {
+  float lo, hi;
+  swap32(x, lo, hi);
+  return fmaxf(lo, hi);
+}
+__device__ __forceinline__ float swap32_sum(float x) {
+  float lo, hi;
+  swap32(x, lo, hi);
+  return lo + hi;
+}
+
 // Convert 8 accumulator values (fp32) to an MFMA operand of element type T.
 __device__ __forceinline__ bf16x8 to_op(const f32x16& v, int off, bf16) {
   bf16x8 r;
@@ -350,6 +378,13 @@ __device__ __forceinline__ typename V8<T>::type zero8() {
   typename V8<T>::type r;
 #pragma unroll
   for (int i = 0; i < 8; ++i) r[i] = (T)0.f;
+  return r;
+}
+template <typename T>
+__device__ __forceinline__ typename V8<T>::type ones8() {
+  typename V8<T>::type r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (T)1.f;
   return r;
 }
 template <typename T>
@@ -457,6 +492,78 @@ __device__ __forceinline__ f32x8 lds_col8(const float* tile, int stride, int k0,
     r[4 + i] = tile[(k0 + 8 + 4 * g + i) * stride + col];
   }
   return r;
+}
+
+// ---- swizzled LDS tiles filled by direct global->LDS loads -----------------
+// A tile of rows of RB bytes is stored unpadded; the 16-byte chunk c of row r
+// sits in chunk slot c ^ sw(r), with sw(r) = (r mod 8) * U (U = chunks per MFMA
+// operand: 1 for bf16, 2 for fp32). Eight consecutive rows read at the same
+// chunk then hit eight different 16-byte bank groups, and an operand's U chunks
+// stay adjacent.
+template <int RB, int U>
+__device__ __forceinline__ int sw_mask(int r) {
+  return ((r & 7) * U) & (RB / 16 - 1);
+}
+
+// LDS byte address of a pointer into __shared__ memory.
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  typedef __attribute__((address_space(3))) const char lds_char;
+  return (unsigned)(unsigned long)(lds_char*)p;
+}
+
+// One global_load_lds_dwordx4: 16 bytes from `base` + `voff` (per lane) to LDS
+// byte `lds` + 16 * lane (lds uniform). It has no register outputs; its
+// completion is waited for with vmcnt. Written as asm because the compiler
+// otherwise drops to lgkmcnt(0) for every LDS read issued while such a copy is
+// in flight; the copies here are waited for with s_waitcnt 0 before the
+// barrier that publishes them. Writing M0 needs one wait state before the load.
+// `base` and `lds` must be the same in every lane (they are read from lane 0).
+__device__ __forceinline__ void lds_dma16(const char* base, unsigned voff, unsigned lds) {
+  const unsigned long long b = (unsigned long long)base;
+  const unsigned blo = __builtin_amdgcn_readfirstlane((unsigned)b);
+  const unsigned bhi = __builtin_amdgcn_readfirstlane((unsigned)(b >> 32));
+  const char* const sbase = (const char*)(((unsigned long long)bhi << 32) | blo);
+  const unsigned slds = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(voff), "s"(sbase), "s"(slds)
+      : "memory");
+}
+
+// Copy R rows of a tile into `lds` with global_load_lds_dwordx4 (no VGPR
+// staging): each wave instruction writes 1 KB of LDS, lane i at byte 16 i, so
+// lane i fetches the chunk that belongs in that slot. Row r of the tile is read
+// at `base` + r * `stride` bytes (base uniform, the per-lane part 32-bit); rows
+// at or past `nvalid` re-read row nvalid - 1. The copies complete
+// asynchronously (vmcnt). 4 waves per workgroup split the instructions.
+template <int R, int RB, int U>
+__device__ __forceinline__ void dma_tile(char* lds, const char* base, unsigned stride, int nvalid,
+                                         int w, int lane) {
+  constexpr int CPR = RB / 16;            // chunks per row
+  constexpr int RPI = 64 / CPR;           // rows per wave instruction
+  constexpr int NI = R / RPI / 4;         // instructions per wave
+  static_assert(NI >= 1 && NI * RPI * 4 == R, "tile does not split over 4 waves");
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int r0 = (w * NI + i) * RPI;
+    const int r = r0 + lane / CPR;
+    const int rr = r < nvalid ? r : nvalid - 1;
+    const unsigned off = (unsigned)rr * stride + 16u * (unsigned)((lane % CPR) ^ sw_mask<RB, U>(r));
+    lds_dma16(base, off, lds_addr(lds + r0 * RB));
+  }
+}
+
+// MFMA operand of 8 consecutive elements (columns col..col+7) of row `row` of a
+// swizzled tile.
+template <typename T, int RB>
+__device__ __forceinline__ typename V8<T>::type lds_sw8(const char* tile, int row, int col) {
+  constexpr int U = 8 * (int)sizeof(T) / 16;
+  const int c = col * (int)sizeof(T) / 16;
+  return *reinterpret_cast<const typename V8<T>::type*>(tile + row * RB +
+                                                       16 * (c ^ sw_mask<RB, U>(row)));
 }
 
 // Row strides (elements) of LDS tiles, chosen against 4-byte bank conflicts:

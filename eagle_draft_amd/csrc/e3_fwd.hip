@@ -23,13 +23,14 @@ struct FwdCfg {
   static constexpr int NT = 256;
   static constexpr int BM = 128;
   static constexpr int BN = 64;
-  static constexpr int KSTR = Stride<T, D>::nat;        // K tile [BN keys][D]
-  static constexpr int VSTR = Stride<T, BN>::nat;       // V^T tile [D][BN keys]
+  static constexpr int KRB = D * (int)sizeof(T);        // K tile [BN keys][D], row bytes
+  static constexpr int VRB = BN * (int)sizeof(T);       // V^T tile [D][BN keys], row bytes
+  static constexpr int U = 8 * (int)sizeof(T) / 16;     // 16-byte chunks per operand
   static constexpr int OSTR = D + 4;       // fp32 staging rows of the epilogue
   static constexpr int KS = D / 16;        // MFMA k-steps over D
   static constexpr int DB = D / 32;        // 32-row blocks of O^T
-  static constexpr int STAGE = (BN * KSTR + D * VSTR) * (int)sizeof(T);
-  static constexpr int LDS_KV = 2 * STAGE;
+  static constexpr int KBYTES = BN * KRB, VBYTES = D * VRB;
+  static constexpr int LDS_KV = 2 * (KBYTES + VBYTES);
   static constexpr int LDS_EPI = 4 * 32 * OSTR * 4 + 2 * BM * 4;
   static constexpr int LDS = LDS_KV > LDS_EPI ? LDS_KV : LDS_EPI;
   static constexpr int NB = sizeof(T) == 2 ? 8 : 2;   // diagonal blocks per epilogue group
@@ -79,79 +80,66 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const Args a) {
   float m_i = kNegInf, l_i = 0.f;
   const float c2 = a.c2;
 
-  auto kbuf = [&](int s) { return reinterpret_cast<T*>(smem + s * C::STAGE); };
-  auto vbuf = [&](int s) { return reinterpret_cast<T*>(smem + s * C::STAGE) + BN * C::KSTR; };  // V^T
-
-  SegIter it;
-  it.begin(geo, lo_min, g_max + 1, BN);
-  TileLoad<T, BN, D, 256> kt;
-  TileLoad<T, D, BN, 256> vt;   // V^T: D rows of BN key positions (zero padded)
-  auto fetch = [&](int s0) {
-    const int nv = a.Tkv - s0;
-    if (nv >= BN) kt.load_full(k0b + (long long)s0 * rs, rs, tid);
-    else kt.load(k0b + (long long)s0 * rs, rs, nv, tid);
-    vt.load_full(vtb + s0, a.kv_pitch, tid);
+  // LDS: two K stages, then two V^T stages, swizzled, filled by direct loads.
+  char* const kb0 = smem;
+  char* const kb1 = kb0 + C::KBYTES;
+  char* const vb0 = kb1 + C::KBYTES;
+  char* const vb1 = vb0 + C::VBYTES;
+  const char* const kbase = reinterpret_cast<const char*>(k0b);
+  const char* const vbase = reinterpret_cast<const char*>(vtb);
+  const unsigned krow = (unsigned)(rs * (long long)sizeof(T));
+  const unsigned vrow = (unsigned)(a.kv_pitch * (long long)sizeof(T));
+  // K rows past the end re-read the last row: those keys are masked.
+  auto dma_k = [&](char* dst, int s0) {
+    const int nv = a.Tkv - s0 < BN ? a.Tkv - s0 : BN;
+    dma_tile<BN, C::KRB, C::U>(dst, kbase + (long long)s0 * krow, krow, nv, w, lane);
   };
-  // Prologue: tile 0 into stage 0, tile 1 into registers.
-  int stage = 0;
-  if (it.valid) {
-    fetch(it.s0);
-    kt.store(kbuf(0), C::KSTR, tid);
-    vt.store(vbuf(0), C::VSTR, tid);
-  }
-  SegIter nx = it;
-  if (nx.valid) nx.next(geo, BN);
-  if (nx.valid) fetch(nx.s0);
-  wait_all();
-  __syncthreads();
+  // V^T rows are the D columns; the copy is zero padded to 64 positions.
+  auto dma_v = [&](char* dst, int s0) {
+    dma_tile<D, C::VRB, C::U>(dst, vbase + (long long)s0 * (long long)sizeof(T), vrow, D, w, lane);
+  };
 
-  while (it.valid) {
-    const int s0 = it.s0, sa = it.a, sb = it.b;
-    const T* Ks = kbuf(stage);
-    const T* Vs = vbuf(stage);
-
-    // S^T for keys [s0, s0+64): two 32-key blocks, lane = query, 16 keys per block.
-    // The two accumulator chains alternate and operands are read a step ahead.
-    f32x16 st[2];
+  // S^T = K Q^T for 64 keys: two 32-key accumulator chains, lane = query.
+  auto qk = [&](const char* Ks, f32x16 (&st)[2]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int j = 0; j < 16; ++j) st[kb][j] = 0.f;
-    {
-      Op a0 = lds_row8(Ks, C::KSTR, l32, 8 * g);
-      Op a1 = lds_row8(Ks, C::KSTR, 32 + l32, 8 * g);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        Op n0 = a0, n1 = a1;
-        if (ks + 1 < KS) {
-          n0 = lds_row8(Ks, C::KSTR, l32, 16 * (ks + 1) + 8 * g);
-          n1 = lds_row8(Ks, C::KSTR, 32 + l32, 16 * (ks + 1) + 8 * g);
-        }
-        mfma16(a0, qreg[ks], st[0]);
-        mfma16(a1, qreg[ks], st[1]);
-        a0 = n0;
-        a1 = n1;
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        mfma16(lds_sw8<T, C::KRB>(Ks, 32 * kb + l32, 16 * ks + 8 * g), qreg[ks], st[kb]);
+  };
+  auto interior = [&](const SegIter& t) {
+    return t.s0 >= t.a && t.s0 + BN <= t.b && t.s0 >= lo_max && t.s0 + BN - 1 <= g_min;
+  };
+  // Key s = t.s0 + 4g + o with o = 32kb + 8(j/4) + j%4 a constant per element;
+  // it is visible to this lane's query when lo <= o <= hi.
+  auto mask = [&](f32x16 (&st)[2], const SegIter& t) {
+    const int base = t.s0 + 4 * g;
+    const int lo = (t.a > loq ? t.a : loq) - base;
+    const int hi = ((t.b - 1) < gq ? (t.b - 1) : gq) - base;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int o = 32 * kb + 8 * (j >> 2) + (j & 3);
+        st[kb][j] = (o >= lo && o <= hi) ? st[kb][j] : kNegInf;
       }
+  };
+  // Row max over the tile (two independent chains), base-2 scaled.
+  auto rowmax = [&](const f32x16 (&st)[2]) {
+    float m0 = kNegInf, m1 = kNegInf;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      m0 = fmaxf(m0, st[0][j]);
+      m1 = fmaxf(m1, st[1][j]);
     }
-    const bool interior = s0 >= sa && s0 + BN <= sb && s0 >= lo_max && s0 + BN - 1 <= g_min;
-    float mx = kNegInf;
-    if (interior) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, st[kb][j]);
-    } else {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int s = s0 + 32 * kb + 8 * (j >> 2) + 4 * g + (j & 3);
-          const bool vis = s >= sa && s < sb && s >= loq && s <= gq;
-          st[kb][j] = vis ? st[kb][j] : kNegInf;
-          mx = fmaxf(mx, st[kb][j]);
-        }
-    }
-    mx = fmaxf(mx, xor32(mx)) * c2;     // this tile's row max, base-2 scaled
+    return swap32_max(fmaxf(m0, m1)) * c2;
+  };
+  // Move the running max when a row's max grew by more than 2^kRescaleSlack.
+  auto rescale = [&](float mx) {
     if (__any(mx > m_i + kRescaleSlack)) {
       const float m_new = fmaxf(m_i, mx);
       const float alpha = m_new == kNegInf ? 1.f : fast_exp2(m_i - m_new);
@@ -162,48 +150,120 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const Args a) {
         for (int j = 0; j < 16; ++j) acc[db][j] *= alpha;
       m_i = m_new;
     }
+  };
+
+  // Step j: S^T(j) is in registers, K(j+1) and V^T(j) are in LDS. The step
+  // first starts the copies of K(j+2) and V^T(j+1) into the stages step j-1
+  // finished with, then overlaps the MFMAs of S^T(j+1) with the exponentials
+  // of tile j, and the MFMAs of O^T += V^T P^T for tile j with the mask and row
+  // max of tile j+1.
+  SegIter it, i1, i2;
+  it.begin(geo, lo_min, g_max + 1, BN);
+  i1 = it;
+  if (i1.valid) i1.next(geo, BN);
+  i2 = i1;
+  if (i2.valid) i2.next(geo, BN);
+  if (it.valid) {
+    dma_k(kb0, it.s0);
+    dma_v(vb0, it.s0);
+  }
+  if (i1.valid) dma_k(kb1, i1.s0);
+  wait_all();
+  __syncthreads();
+
+  f32x16 sa[2], sb[2];
+  if (it.valid) {
+    qk(kb0, sa);
+    if (!interior(it)) mask(sa, it);
+    rescale(rowmax(sa));
+  }
+  __syncthreads();   // K(0) is read; the first step overwrites its stage
+  const Op ones = ones8<T>();
+
+  auto step = [&](f32x16 (&sc)[2], f32x16 (&sn)[2], const char* Kn, const char* Vc, char* Kw,
+                  char* Vw) {
+    if (i2.valid) dma_k(Kw, i2.s0);
+    if (i1.valid) dma_v(Vw, i1.s0);
+    // Phase A: S^T(j+1) on MFMA (stale LDS when there is no tile j+1: the
+    // result is then never used); P(j) and its row sum on VALU. The order is
+    // fixed by scheduling fences: in step i the K operand of MFMA i+2 is read,
+    // MFMA i issues, and 2 of the 32 exponentials of this lane are computed.
     const float nb = m_i == kNegInf ? 0.f : -m_i;
+    Op pv[BN / 16];
     float rsum = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const float p = fast_exp2(fmaf(st[kb][j], c2, nb));
-        st[kb][j] = p;
-        rsum += p;
-      }
-    l_i += rsum;
-    // O^T += V^T P^T over the 64 keys (4 k-steps of 16).
     {
-      Op pv[BN / 16];
 #pragma unroll
-      for (int ks = 0; ks < BN / 16; ++ks) pv[ks] = to_op(st[ks >> 1], 8 * (ks & 1), T());
-      Op va[DB];
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int db = 0; db < DB; ++db) va[db] = lds_row8(Vs, C::VSTR, 32 * db + l32, 8 * g);
+        for (int j = 0; j < 16; ++j) sn[kb][j] = 0.f;
+      constexpr int NQ = 2 * KS;                 // MFMAs: i = 2 ks + kb
+      Op ka[3];
+      ka[0] = lds_sw8<T, C::KRB>(Kn, l32, 8 * g);
+      ka[1] = lds_sw8<T, C::KRB>(Kn, 32 + l32, 8 * g);
+#pragma unroll
+      for (int i = 0; i < NQ; ++i) {
+        if (i + 2 < NQ)
+          ka[(i + 2) % 3] = lds_sw8<T, C::KRB>(Kn, 32 * ((i + 2) & 1) + l32, 16 * ((i + 2) >> 1) + 8 * g);
+        mfma16(ka[i % 3], qreg[i >> 1], sn[i & 1]);
+        // Exponentials: 32 per lane over the NQ steps.
+#pragma unroll
+        for (int e = (32 * i) / NQ; e < (32 * (i + 1)) / NQ; ++e)
+          sc[e >> 4][e & 15] = fast_exp2(fmaf(sc[e >> 4][e & 15], c2, nb));
+        // Every 8 exponentials: one bf16 operand and its part of the row sum.
+        // (pinned here: otherwise they sink past the mask branch below, away
+        // from the MFMAs they overlap).
+#pragma unroll
+        for (int q = 0; q < BN / 16; ++q)
+          if ((32 * (i + 1)) / NQ >= 8 * (q + 1) && (32 * i) / NQ < 8 * (q + 1)) {
+            pv[q] = to_op(sc[q >> 1], 8 * (q & 1), T());
+            rsum = dot8(pv[q], ones, rsum);
+            pin(pv[q]);
+            pin(rsum);
+          }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    l_i += rsum;
+    if (i1.valid && !interior(i1)) mask(sn, i1);
+    // Phase B: O^T += V^T(j) P^T(j) on MFMA, operands read one k-step ahead;
+    // the row max of tile j+1 on VALU, a quarter per k-step.
+    float mx0 = kNegInf, mx1 = kNegInf;
+    {
+      Op va[2][DB];
+#pragma unroll
+      for (int db = 0; db < DB; ++db) va[0][db] = lds_sw8<T, C::VRB>(Vc, 32 * db + l32, 8 * g);
 #pragma unroll
       for (int ks = 0; ks < BN / 16; ++ks) {
+        if (ks + 1 < BN / 16) {
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const Op cur = va[db];
-          if (ks + 1 < BN / 16) va[db] = lds_row8(Vs, C::VSTR, 32 * db + l32, 16 * (ks + 1) + 8 * g);
-          mfma16(cur, pv[ks], acc[db]);
+          for (int db = 0; db < DB; ++db)
+            va[(ks + 1) & 1][db] = lds_sw8<T, C::VRB>(Vc, 32 * db + l32, 16 * (ks + 1) + 8 * g);
         }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) mfma16(va[ks & 1][db], pv[ks], acc[db]);
+#pragma unroll
+        for (int j = 4 * ks; j < 4 * ks + 4; ++j) {
+          mx0 = fmaxf(mx0, sn[0][j]);
+          mx1 = fmaxf(mx1, sn[1][j]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
-
-    // Next tile: registers -> the other stage; fetch the one after.
-    it = nx;
-    if (it.valid) {
-      kt.store(kbuf(stage ^ 1), C::KSTR, tid);
-      vt.store(vbuf(stage ^ 1), C::VSTR, tid);
-      nx.next(geo, BN);
-      if (nx.valid) fetch(nx.s0);
-    }
-    stage ^= 1;
+    const float mx = swap32_max(fmaxf(mx0, mx1)) * c2;
+    if (i1.valid) rescale(mx);
+    it = i1;
+    i1 = i2;
+    if (i2.valid) i2.next(geo, BN);
+    wait_all();
     __syncthreads();
+  };
+  while (it.valid) {
+    step(sa, sb, kb1, vb0, kb0, vb1);
+    if (!it.valid) break;
+    step(sb, sa, kb0, vb1, kb1, vb0);
   }
-  l_i += xor32(l_i);
+  l_i = swap32_sum(l_i);
 
   // ---- epilogue: stage O^T (unnormalised), m, l through LDS ----------------
   float* Ow = reinterpret_cast<float*>(smem) + w * 32 * C::OSTR;

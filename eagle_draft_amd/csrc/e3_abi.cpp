@@ -184,6 +184,23 @@ int fwd_impl(const e3_problem* p, const void* q, const void* k0, const void* v0,
   return ok();
 }
 
+struct BwdWs {
+  int pitch;
+  size_t delta, qt, dot, total;
+};
+
+BwdWs bwd_ws_layout(const e3_problem* p) {
+  BwdWs l;
+  l.pitch = geo_of(p).qruns().pitch;
+  const size_t esz = p->dtype == E3_BF16 ? 2 : 4;
+  const size_t rows = (size_t)p->B * p->H * l.pitch;       // multiple of 64
+  l.delta = rows * sizeof(float);
+  l.qt = 2 * rows * sizeof(float);
+  l.dot = l.qt + rows * p->D * esz;
+  l.total = l.dot + rows * p->D * esz;
+  return l;
+}
+
 int bwd_impl(const e3_problem* p, const void* dout, const void* q, const void* k0, const void* v0,
              const void* kd, const void* vd, const void* out, const float* lse, void* ws, void* dq,
              void* dk0, void* dv0, void* dkd, void* dvd, hipStream_t st, bool whole) {
@@ -211,7 +228,17 @@ int bwd_impl(const e3_problem* p, const void* dout, const void* q, const void* k
   a.dout = dout;
   a.o_in = out;
   a.lse_in = lse;
-  a.delta = static_cast<float*>(ws);
+  {
+    // workspace: lse2, delta (float [B,H,P]), then Q^T and dO^T (dtype [B,H,D,P]),
+    // P = the 64-aligned per-run row layout of the local queries.
+    const BwdWs l = bwd_ws_layout(p);
+    char* w = static_cast<char*>(ws);
+    a.q_pitch = l.pitch;
+    a.lse2 = reinterpret_cast<float*>(w);
+    a.delta = reinterpret_cast<float*>(w + l.delta);
+    a.qt = w + l.qt;
+    a.dot = w + l.dot;
+  }
   a.dq = dq;
   a.dk0 = dk0;
   a.dv0 = dv0;
@@ -251,8 +278,8 @@ size_t eagle3_bwd_workspace_bytes(const e3_problem* p) {
   Resolved r;
   if (validate(p, r, false, false)) return 0;
   g_err.clear();
-  const size_t n = (size_t)p->B * p->H * p->T * sizeof(float);
-  return (n + 255) & ~(size_t)255;
+  if (p->T == 0) return 0;
+  return bwd_ws_layout(p).total;
 }
 
 size_t eagle3_fwd_workspace_bytes(const e3_problem* p) {

@@ -6,13 +6,17 @@
 // probabilities are P = exp(scale*q.k - lse) with the lse that includes the diagonal
 // blocks, and the diagonal gradients follow in closed form.
 //
-// Three kernels, no atomics (every output element has one writer):
-//   delta_kernel  delta[b,h,t] = <dO_t, O_t> (O = the stored merged out)
+// Kernels, no atomics (every output element has one writer):
+//   delta_kernel  delta[b,h,t] = <dO_t, O_t> (O = the stored merged out) and
+//                 lse2 = lse * log2(e), in the 64-aligned per-run row layout
+//   xpose (x2)    Q^T and dO^T copies (e3_xpose.hip) for the dK/dV operands
 //   dkdv_kernel   one workgroup per 128 block-0 keys (32 per wave, lane = key);
 //                 loops over the query tiles that see them:
 //                   S = Q K^T, P, dP = dO V^T, dS = P (dP - delta),
 //                   dV += P^T dO, dK += scale dS^T Q
-//                 Q and dO tiles are staged in LDS both as-is and transposed.
+//                 Q / dO tiles and their transposes stream through swizzled
+//                 LDS stages filled by direct global->LDS copies; the S / dP
+//                 MFMAs of tile j+1 overlap the P / dS arithmetic of tile j.
 //   dq_kernel     one workgroup per 128 query rows (lane = query, as in the
 //                 forward); loops over the visible key tiles in ring order:
 //                   dQ += dS K; then the epilogue adds the diagonal terms
@@ -23,27 +27,35 @@
 namespace e3 {
 
 // ---------------------------------------------------------------------------
-// delta = rowsum(dO * O)
+// delta = rowsum(dO * O), lse2 = lse * log2(e); one row per LPR lanes, rows in
+// the padded layout [b][h][p] (padding positions get 0)
 // ---------------------------------------------------------------------------
 template <typename T, int D>
 __global__ __launch_bounds__(256) void delta_kernel(const Args a) {
   constexpr int LPR = D / 8;
-  constexpr int RPB = 256 / LPR;   // rows (b, t, h) per block
+  constexpr int RPB = 256 / LPR;   // rows per block
+  const Geo geo{a.layout, a.cp, a.rank, a.T, a.Tkv};
   const int lane = threadIdx.x;
-  const long long r = (long long)blockIdx.x * RPB + lane / LPR;   // row over B*T*H
-  const long long nrow = (long long)a.B * a.T * a.H;
+  const int qp = a.q_pitch;
+  const long long r = (long long)blockIdx.x * RPB + lane / LPR;   // over B*H*qp
+  const long long nrow = (long long)a.B * a.H * qp;
   const bool valid = r < nrow;
   const long long rr = valid ? r : 0;
+  const int bh = (int)(rr / qp), p = (int)(rr % qp), b = bh / a.H, h = bh % a.H;
+  const int t = geo.trow(p);
   const int cc = (lane % LPR) * 8;
-  const f32x8 x = load8f(reinterpret_cast<const T*>(a.dout) + rr * D + cc);
-  const f32x8 y = load8f(reinterpret_cast<const T*>(a.o_in) + rr * D + cc);
   float d = 0.f;
+  if (t >= 0) {
+    const long long off = (((long long)b * a.T + t) * a.H + h) * D + cc;
+    const f32x8 x = load8f(reinterpret_cast<const T*>(a.dout) + off);
+    const f32x8 y = load8f(reinterpret_cast<const T*>(a.o_in) + off);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) d += x[e] * y[e];
+    for (int e = 0; e < 8; ++e) d += x[e] * y[e];
+  }
   d = group_sum<LPR>(d);
   if (valid && (lane % LPR) == 0) {
-    const long long h = rr % a.H, bt = rr / a.H, t = bt % a.T, b = bt / a.T;
-    a.delta[(b * a.H + h) * a.T + t] = d;
+    a.delta[rr] = d;
+    a.lse2[rr] = t >= 0 ? a.lse_in[(long long)bh * a.T + t] * kLog2e : 0.f;
   }
 }
 
@@ -53,12 +65,20 @@ __global__ __launch_bounds__(256) void delta_kernel(const Args a) {
 template <typename T, int D>
 struct DkdvCfg {
   static constexpr int BNK = 128;            // keys per workgroup (32 per wave)
-  static constexpr int BMQ = 64;             // query rows per iteration
-  static constexpr int STR = Stride<T, D>::both;   // Q and dO tiles are read both ways
+  static constexpr int BMQ = 32;            // queries per step
+  static constexpr int MB = BMQ / 32;        // 32-query blocks per step
   static constexpr int KS = D / 16;
   static constexpr int DB = D / 32;
-  static constexpr int STAGE = 2 * BMQ * STR * (int)sizeof(T) + 2 * BMQ * 4;
-  static constexpr int LDS = 2 * STAGE;
+  static constexpr int U = 8 * (int)sizeof(T) / 16;     // 16-byte chunks per operand
+  static constexpr int RRB = D * (int)sizeof(T);        // row tiles Q, dO [BMQ][D]: row bytes
+  static constexpr int CRB = BMQ * (int)sizeof(T);      // column tiles Q^T, dO^T [D][BMQ]
+  static constexpr int RT = BMQ * RRB, CT = D * CRB;     // bytes per tile
+  static constexpr int RSTAGE = 2 * RT;                 // Q, dO
+  static constexpr int CSTAGE = 2 * CT;                 // Q^T, dO^T
+  static constexpr int LSTAGE = 2 * BMQ * 4;            // lse2, delta
+  // The tile stages come first so that every operand read addresses them with
+  // one lane register and an immediate offset (below 64 KB).
+  static constexpr int LDS = 2 * RSTAGE + 2 * CSTAGE + 2 * LSTAGE;
 };
 
 // Query tiles (rows of the share) that can see keys [k_lo, k_hi) with document
@@ -104,13 +124,22 @@ template <typename T, int D>
 __global__ __launch_bounds__(256, 1) void dkdv_kernel(const Args a) {
   using C = DkdvCfg<T, D>;
   using Op = typename V8<T>::type;
-  constexpr int BNK = C::BNK, BMQ = C::BMQ, KS = C::KS, DB = C::DB, STR = C::STR;
+  constexpr int BNK = C::BNK, BMQ = C::BMQ, MB = C::MB, KS = C::KS, DB = C::DB;
+  constexpr int sz = (int)sizeof(T);
   __shared__ __attribute__((aligned(16))) char smem[C::LDS];
-  auto qbuf = [&](int s) { return reinterpret_cast<T*>(smem + s * C::STAGE); };
-  auto obuf = [&](int s) { return reinterpret_cast<T*>(smem + s * C::STAGE) + BMQ * STR; };
-  auto lbuf = [&](int s) { return reinterpret_cast<float*>(smem + s * C::STAGE + 2 * BMQ * STR * (int)sizeof(T)); };
+  // Row stages hold Q at 0 and dO at RT; column stages hold Q^T at 0 and dO^T
+  // at CT; each column stage has an lse2 / delta stage (BMQ floats each).
+  char* const rb0 = smem;
+  char* const rb1 = rb0 + C::RSTAGE;
+  char* const cb0 = rb1 + C::RSTAGE;
+  char* const cb1 = cb0 + C::CSTAGE;
+  char* const lb0 = cb1 + C::CSTAGE;
+  auto lstage = [&](const char* cb) { return lb0 + (cb == cb0 ? 0 : C::LSTAGE); };
+  const unsigned sbase = lds_addr(smem);
+  auto la = [&](const char* p) { return sbase + (unsigned)(p - smem); };
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int BH = a.B * a.H;
   const int kt = tile_order(blockIdx.x / BH, (a.Tkv + BNK - 1) / BNK), bh = blockIdx.x % BH,
             b = bh / a.H, h = bh % a.H;
@@ -121,10 +150,16 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const Args a) {
   const long long rs = (long long)a.H * D;
   const T* k0b = reinterpret_cast<const T*>(a.k0) + (long long)b * a.k0_bs + (long long)h * D;
   const T* v0b = reinterpret_cast<const T*>(a.v0) + (long long)b * a.k0_bs + (long long)h * D;
-  const T* qb = reinterpret_cast<const T*>(a.q) + (long long)b * a.T * rs + (long long)h * D;
-  const T* dob = reinterpret_cast<const T*>(a.dout) + (long long)b * a.T * rs + (long long)h * D;
-  const float* lseb = a.lse_in + ((long long)b * a.H + h) * a.T;
-  const float* delb = a.delta + ((long long)b * a.H + h) * a.T;
+  const char* const qbytes =
+      reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.q) + (long long)b * a.T * rs + (long long)h * D);
+  const char* const obytes =
+      reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.dout) + (long long)b * a.T * rs + (long long)h * D);
+  const long long cbase = (long long)bh * D * a.q_pitch;
+  const char* const qtbytes = reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.qt) + cbase);
+  const char* const otbytes = reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.dot) + cbase);
+  const char* const lbytes = reinterpret_cast<const char*>(a.lse2 + (long long)bh * a.q_pitch);
+  const unsigned ldoff = (unsigned)((long long)BH * a.q_pitch * 4);   // lse2 -> delta
+  const unsigned rrow = (unsigned)(rs * sz), crow = (unsigned)((long long)a.q_pitch * sz);
 
   // This lane's key; a query at global position gm sees it iff s <= gm < s_hi.
   const int s = kt0 + w * 32 + l32;
@@ -149,107 +184,207 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const Args a) {
     }
   const float c2 = a.c2;
 
-  QIter it;
-  it.begin(geo, kt0, q_hi, BMQ);
-  TileLoad<T, BMQ, D, 256> qt, ot;
-  float lv = 0.f, dl = 0.f;
-  auto fetch = [&](const QIter& q) {
+  auto dma_rows = [&](char* dst, const QIter& q) {
     const int r0 = q.row0(), nr = q.nrows(BMQ);
-    if (nr == BMQ) {
-      qt.load_full(qb + (long long)r0 * rs, rs, tid);
-      ot.load_full(dob + (long long)r0 * rs, rs, tid);
-    } else {
-      qt.load(qb + (long long)r0 * rs, rs, nr, tid);
-      ot.load(dob + (long long)r0 * rs, rs, nr, tid);
-    }
-    if (tid < BMQ) {
-      lv = tid < nr ? lseb[r0 + tid] * kLog2e : 0.f;
-      dl = tid < nr ? delb[r0 + tid] : 0.f;
+    dma_tile<BMQ, C::RRB, C::U>(la(dst), qbytes + (long long)r0 * rrow, rrow, nr, w, lane);
+    dma_tile<BMQ, C::RRB, C::U>(la(dst) + C::RT, obytes + (long long)r0 * rrow, rrow, nr, w, lane);
+  };
+  auto dma_cols = [&](char* dst, const QIter& q) {
+    const int p0 = geo.prow(q.row0());
+    dma_tile<D, C::CRB, C::U>(la(dst), qtbytes + (long long)p0 * sz, crow, D, w, lane);
+    dma_tile<D, C::CRB, C::U>(la(dst) + C::CT, otbytes + (long long)p0 * sz, crow, D, w, lane);
+    if (w == 0 && lane < BMQ / 2) {
+      const unsigned voff = lane < BMQ / 4 ? 16u * lane : ldoff + 16u * (lane - BMQ / 4);
+      lds_dma16(lbytes + (long long)p0 * 4, voff, la(lstage(dst)));
     }
   };
-  auto put = [&](int st) {
-    qt.store(qbuf(st), STR, tid);
-    ot.store(obuf(st), STR, tid);
-    if (tid < BMQ) {
-      lbuf(st)[tid] = lv;
-      lbuf(st)[BMQ + tid] = dl;
-    }
-  };
-  int stage = 0;
-  if (it.valid) {
-    fetch(it);
-    put(0);
-  }
-  QIter nx = it;
-  if (nx.valid) nx.next(geo, BMQ);
-  if (nx.valid) fetch(nx);
-  wait_all();
-  __syncthreads();
-
-  while (it.valid) {
-    const int nr = it.nrows(BMQ), gq0 = it.gpos0();
-    const T* Qs = qbuf(stage);
-    const T* Os = obuf(stage);
-    const float* L2s = lbuf(stage);
-    const float* Ds = L2s + BMQ;
-
-    // S = Q K^T and dP = dO V^T: two 32-query blocks, lane = key, 16 queries each.
-    f32x16 sp[2], dp[2];
+  // S^T-like scores and dP for a row stage: lane = key, 16 queries per block.
+  auto sdp = [&](const char* R, f32x16 (&sp)[MB], f32x16 (&dp)[MB]) {
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         sp[mb][j] = 0.f;
         dp[mb][j] = 0.f;
       }
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        mfma16(lds_row8(Qs, STR, 32 * mb + l32, 16 * ks + 8 * g), kreg[ks], sp[mb]);
-        mfma16(lds_row8(Os, STR, 32 * mb + l32, 16 * ks + 8 * g), vreg[ks], dp[mb]);
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        mfma16(lds_sw8<T, C::RRB>(R, 32 * mb + l32, 16 * ks + 8 * g), kreg[ks], sp[mb]);
+        mfma16(lds_sw8<T, C::RRB>(R + C::RT, 32 * mb + l32, 16 * ks + 8 * g), vreg[ks], dp[mb]);
       }
-    }
-    const bool interior = nr == BMQ && kt0 + BNK <= a.Tkv && gq0 >= kt0 + BNK - 1 &&
-                          gq0 + BMQ - 1 < hi_min;
+  };
+  auto interior = [&](const QIter& q) {
+    const int gq0 = q.gpos0();
+    return q.nrows(BMQ) == BMQ && kt0 + BNK <= a.Tkv && gq0 >= kt0 + BNK - 1 &&
+           gq0 + BMQ - 1 < hi_min;
+  };
+  // Query m of the tile (m = 4g + o, o = 32mb + 8(j/4) + j%4 a constant per
+  // element) sees this lane's key when mlo <= m <= mhi.
+  auto mask = [&](f32x16 (&sp)[MB], const QIter& q) {
+    const int gq0 = q.gpos0(), nr = q.nrows(BMQ);
+    const int lo = s - gq0 - 4 * g;
+    const int hi = (svalid ? ((nr < s_hi - gq0 ? nr : s_hi - gq0) - 1) : -1) - 4 * g;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int m0 = 32 * mb + 8 * jj + 4 * g;
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(L2s + m0);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(Ds + m0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int j = 4 * jj + i;
-          float p = fast_exp2(fmaf(sp[mb][j], c2, -l4[i]));
-          if (!interior) {
-            const int m = m0 + i, gm = gq0 + m;
-            const bool vis = svalid && m < nr && gm >= s && gm < s_hi;
-            p = vis ? p : 0.f;
-          }
-          sp[mb][j] = p;
-          dp[mb][j] = p * (dp[mb][j] - d4[i]);
-        }
+      for (int j = 0; j < 16; ++j) {
+        const int o = 32 * mb + 8 * (j >> 2) + (j & 3);
+        sp[mb][j] = (o >= lo && o <= hi) ? sp[mb][j] : kNegInf;
       }
-    // dV^T += dO^T P, dK^T += Q^T dS over the 64 queries (4 k-steps of 16).
-#pragma unroll
-    for (int ks = 0; ks < BMQ / 16; ++ks) {
-      const Op pb = to_op(sp[ks >> 1], 8 * (ks & 1), T());
-      const Op sb = to_op(dp[ks >> 1], 8 * (ks & 1), T());
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        mfma16(lds_col8(Os, STR, 16 * ks, 32 * db, lane), pb, dv[db]);
-        mfma16(lds_col8(Qs, STR, 16 * ks, 32 * db, lane), sb, dk[db]);
-      }
-    }
+  };
 
-    it = nx;
-    if (it.valid) {
-      put(stage ^ 1);
-      nx.next(geo, BMQ);
-      if (nx.valid) fetch(nx);
+  QIter it, i1, i2;
+  it.begin(geo, kt0, q_hi, BMQ);
+  i1 = it;
+  if (i1.valid) i1.next(geo, BMQ);
+  i2 = i1;
+  if (i2.valid) i2.next(geo, BMQ);
+  if (it.valid) {
+    dma_rows(rb0, it);
+    dma_cols(cb0, it);
+  }
+  if (i1.valid) dma_rows(rb1, i1);
+  wait_all();
+  __syncthreads();
+  f32x16 sa[MB], da[MB], sb[MB], dbb[MB];
+  if (it.valid) sdp(rb0, sa, da);
+  __syncthreads();   // the first step overwrites row stage 0
+
+  // Step j: S(j), dP(j) in registers; rows of tile j+1 and columns of tile j in
+  // LDS. Starts the copies of rows(j+2) and columns(j+1) into the stages step
+  // j-1 finished with. Phase A: S, dP of tile j+1 on MFMA while P(j), dS(j) are
+  // formed on VALU; phase B: dV += dO^T P, dK += Q^T dS for tile j.
+  auto step = [&](f32x16 (&sc)[MB], f32x16 (&dc)[MB], f32x16 (&sn)[MB], f32x16 (&dn)[MB],
+                  const char* Rn, const char* Cc, char* Rw, char* Cw) {
+    // Copies of rows(j+2) and columns(j+1), one instruction at a time between
+    // the phase A MFMAs (a missing tile re-copies the current one into the free
+    // stage, so the sequence has no branches).
+    constexpr int NR = DmaShape<BMQ, C::RRB>::NI, NC = DmaShape<D, C::CRB>::NI;
+    constexpr int NDMA = 2 * NR + 2 * NC + 1;
+    const int dr0 = (i2.valid ? i2 : it).row0(), dnr = (i2.valid ? i2 : it).nrows(BMQ);
+    const int dp0 = geo.prow((i1.valid ? i1 : it).row0());
+    const unsigned lrw = la(Rw), lcw = la(Cw);
+    auto dma_part = [&](int k) {
+      if (k < NR) {
+        dma_tile_part<BMQ, C::RRB, C::U>(lrw, qbytes + (long long)dr0 * rrow, rrow, dnr, w, lane, k);
+      } else if (k < 2 * NR) {
+        dma_tile_part<BMQ, C::RRB, C::U>(lrw + C::RT, obytes + (long long)dr0 * rrow, rrow, dnr, w, lane, k - NR);
+      } else if (k < 2 * NR + NC) {
+        dma_tile_part<D, C::CRB, C::U>(lcw, qtbytes + (long long)dp0 * sz, crow, D, w, lane, k - 2 * NR);
+      } else if (k < 2 * NR + 2 * NC) {
+        dma_tile_part<D, C::CRB, C::U>(lcw + C::CT, otbytes + (long long)dp0 * sz, crow, D, w, lane,
+                                       k - 2 * NR - NC);
+      } else if (w == 0 && lane < BMQ / 2) {
+        const unsigned voff = lane < BMQ / 4 ? 16u * lane : ldoff + 16u * (lane - BMQ / 4);
+        lds_dma16(lbytes + (long long)dp0 * 4, voff, la(lstage(Cw)));
+      }
+    };
+    if (!interior(it)) mask(sc, it);
+    const float* L2s = reinterpret_cast<const float*>(lstage(Cc));
+    const float* Ds = L2s + BMQ;
+    // lse2 / delta of the tile's queries, 4 at a time (group e/4 of the lane's
+    // elements), read one group ahead.
+    auto ld4 = [&](int grp, f32x4& l, f32x4& d) {
+      const int off = 32 * (grp >> 2) + 8 * (grp & 3) + 4 * g;
+      l = *reinterpret_cast<const f32x4*>(L2s + off);
+      d = *reinterpret_cast<const f32x4*>(Ds + off);
+    };
+    // Phase A. MFMA i: ks = i / (2 MB), block mb, S (even) or dP (odd); its
+    // A operand is read two MFMAs ahead. E elements of P / dS per lane spread
+    // over the NQ steps.
+    Op pb[BMQ / 16], sbo[BMQ / 16];
+    {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          sn[mb][j] = 0.f;
+          dn[mb][j] = 0.f;
+        }
+      constexpr int NQ = 2 * MB * KS, E = 16 * MB;
+      auto opnd = [&](int i) {
+        const int ks = i / (2 * MB), mb = (i / 2) % MB;
+        return lds_sw8<T, C::RRB>(Rn + (i & 1) * C::RT, 32 * mb + l32, 16 * ks + 8 * g);
+      };
+      Op ka[3];
+      ka[0] = opnd(0);
+      ka[1] = opnd(1);
+      f32x4 lg[2], dg[2];
+      ld4(0, lg[0], dg[0]);
+#pragma unroll
+      for (int i = 0; i < NQ; ++i) {
+        if (i + 2 < NQ) ka[(i + 2) % 3] = opnd(i + 2);
+        {
+          const int ks = i / (2 * MB), mb = (i / 2) % MB;
+          if (i & 1) mfma16(ka[i % 3], vreg[ks], dn[mb]);
+          else mfma16(ka[i % 3], kreg[ks], sn[mb]);
+        }
+#pragma unroll
+        for (int k = (NDMA * i + NQ - 1) / NQ; k < (NDMA * (i + 1) + NQ - 1) / NQ; ++k) dma_part(k);
+#pragma unroll
+        for (int e = (E * i) / NQ; e < (E * (i + 1)) / NQ; ++e) {
+          const int mb = e >> 4, j = e & 15, grp = e >> 2;
+          if ((e & 3) == 0 && grp + 1 < E / 4) ld4(grp + 1, lg[(grp + 1) & 1], dg[(grp + 1) & 1]);
+          const float p = fast_exp2(fmaf(sc[mb][j], c2, -lg[grp & 1][j & 3]));
+          sc[mb][j] = p;
+          dc[mb][j] = p * (dc[mb][j] - dg[grp & 1][j & 3]);
+        }
+#pragma unroll
+        for (int q = 0; q < BMQ / 16; ++q)
+          if ((E * (i + 1)) / NQ >= 8 * (q + 1) && (E * i) / NQ < 8 * (q + 1)) {
+            pb[q] = to_op(sc[q >> 1], 8 * (q & 1), T());
+            sbo[q] = to_op(dc[q >> 1], 8 * (q & 1), T());
+            pin(pb[q]);
+            pin(sbo[q]);
+          }
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
-    stage ^= 1;
+    // Phase B: dV^T += dO^T P^T and dK^T += Q^T dS^T over the BMQ queries.
+    // Step k = (ks, db) issues the two MFMAs of one 32-row block of D; its
+    // operands are read two steps ahead.
+    {
+      constexpr int NK = (BMQ / 16) * DB;
+      auto vop = [&](int k) {
+        return lds_sw8<T, C::CRB>(Cc + C::CT, 32 * (k % DB) + l32, 16 * (k / DB) + 8 * g);
+      };
+      auto qop = [&](int k) {
+        return lds_sw8<T, C::CRB>(Cc, 32 * (k % DB) + l32, 16 * (k / DB) + 8 * g);
+      };
+      Op va[3], qa[3];
+      va[0] = vop(0);
+      qa[0] = qop(0);
+      va[1] = vop(1);
+      qa[1] = qop(1);
+#pragma unroll
+      for (int k = 0; k < NK; ++k) {
+        if (k + 2 < NK) {
+          va[(k + 2) % 3] = vop(k + 2);
+          qa[(k + 2) % 3] = qop(k + 2);
+        }
+        mfma16(va[k % 3], pb[k / DB], dv[k % DB]);
+        mfma16(qa[k % 3], sbo[k / DB], dk[k % DB]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // The next tile's S / dP become the current ones (accumulator -> VALU registers).
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      sc[mb] = sn[mb];
+      dc[mb] = dn[mb];
+    }
+    it = i1;
+    i1 = i2;
+    if (i2.valid) i2.next(geo, BMQ);
+    wait_all();
     __syncthreads();
+  };
+  // One step per iteration; the stages alternate with the step parity.
+  for (int par = 0; it.valid; par ^= 1) {
+    const int odd = __builtin_amdgcn_readfirstlane(par);
+    step(sa, da, sb, dbb, odd ? rb0 : rb1, odd ? cb1 : cb0, odd ? rb1 : rb0, odd ? cb0 : cb1);
   }
 
   // Write dK0 = scale * dK, dV0 (rows of keys no query sees are zeros).
@@ -318,8 +453,9 @@ __global__ __launch_bounds__(256, E3_DQ_OCC) void dq_kernel(const Args a) {
   const T* dob = reinterpret_cast<const T*>(a.dout) + (long long)b * a.T * rs + (long long)h * D;
   const T* k0b = reinterpret_cast<const T*>(a.k0) + (long long)b * a.k0_bs + (long long)h * D;
   const T* v0b = reinterpret_cast<const T*>(a.v0) + (long long)b * a.k0_bs + (long long)h * D;
-  const float* lseb = a.lse_in + ((long long)b * a.H + h) * a.T;
-  const float* delb = a.delta + ((long long)b * a.H + h) * a.T;
+  // lse2 / delta rows in the padded layout; the tile lies inside one run.
+  const float* lseb = a.lse2 + (long long)bh * a.q_pitch + (geo.prow(row0) - row0);
+  const float* delb = a.delta + (long long)bh * a.q_pitch + (geo.prow(row0) - row0);
 
   const int qr = w * 32 + l32;
   const bool qvalid = qr < nrows;
@@ -328,7 +464,7 @@ __global__ __launch_bounds__(256, E3_DQ_OCC) void dq_kernel(const Args a) {
   const int g_min = gpos0, g_max = gpos0 + nrows - 1;
   const int lo_min = doc_lo_of(a.cu, a.ndocs, g_min);
   const int lo_max = doc_lo_of(a.cu, a.ndocs, g_max);
-  const float lq = qvalid ? lseb[row0 + qr] * kLog2e : 0.f;
+  const float lq = qvalid ? lseb[row0 + qr] : 0.f;
   const float dq_delta = qvalid ? delb[row0 + qr] : 0.f;
 
   Op qreg[KS], oreg[KS];
@@ -457,7 +593,7 @@ __global__ __launch_bounds__(256, E3_DQ_OCC) void dq_kernel(const Args a) {
     f32x8 dqv = *reinterpret_cast<const f32x8*>(Qw + rr * C::OSTR + cc);
     const V qv = load8(qb + row * rs + cc);
     const V ov = load8(dob + row * rs + cc);
-    const float l2 = lseb[row] * kLog2e;
+    const float l2 = lseb[row];
     const float dl = delb[row];
     for (int i0 = 0; i0 < a.N; i0 += NB) {
       const int n = (a.N - i0) < NB ? (a.N - i0) : NB;
@@ -501,29 +637,41 @@ __global__ __launch_bounds__(256, E3_DQ_OCC) void dq_kernel(const Args a) {
 
 template <typename T, int D>
 static hipError_t launch_bwd_t(const Args& a, hipStream_t st) {
-  const long long nrow = (long long)a.B * a.T * a.H;
+  const Geo geo{a.layout, a.cp, a.rank, a.T, a.Tkv};
+  const long long nrow = (long long)a.B * a.H * a.q_pitch;
+  if (nrow == 0) return hipSuccess;
   timing_mark(st);
-  if (nrow > 0) {
+  {
     const long long nb = (nrow + (256 / (D / 8)) - 1) / (256 / (D / 8));
     hipLaunchKernelGGL((delta_kernel<T, D>), dim3((unsigned)nb), dim3(256), 0, st, a);
-    timing_mark(st);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  timing_mark(st);
+  {
+    const long long qbs = (long long)a.T * a.H * D;
+    hipError_t e = launch_xpose(a.q, qbs, const_cast<void*>(a.qt), geo.qruns(), a.B, a.H,
+                                sizeof(T) == 2 ? 0 : 1, D, st);
+    if (e == hipSuccess)
+      e = launch_xpose(a.dout, qbs, const_cast<void*>(a.dot), geo.qruns(), a.B, a.H,
+                       sizeof(T) == 2 ? 0 : 1, D, st);
+    if (e != hipSuccess) return e;
+  }
+  timing_mark(st);
   const long long nk = (long long)((a.Tkv + DkdvCfg<T, D>::BNK - 1) / DkdvCfg<T, D>::BNK) * a.B * a.H;
   if (nk > 0) {
     hipLaunchKernelGGL((dkdv_kernel<T, D>), dim3((unsigned)nk), dim3(256), 0, st, a);
-    timing_mark(st);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const Geo geo{a.layout, a.cp, a.rank, a.T, a.Tkv};
+  timing_mark(st);
   const long long nq = (long long)geo.ntiles(DqCfg<T, D>::BM) * a.B * a.H;
   if (nq > 0) {
     hipLaunchKernelGGL((dq_kernel<T, D>), dim3((unsigned)nq), dim3(256), 0, st, a);
-    timing_mark(st);
-    return hipGetLastError();
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
+  timing_mark(st);
   return hipSuccess;
 }
 

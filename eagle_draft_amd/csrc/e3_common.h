@@ -34,7 +34,8 @@ struct Args {
   const float* lse_in;  // merged lse (backward input)
   void* out;
   float* lse;
-  float* delta;         // rowsum(dO * O), [B, H, T]
+  float* delta;         // rowsum(dO * O), [B, H, q_pitch] (rows at Geo::prow)
+  float* lse2;          // lse * log2(e), same layout as delta (delta = lse2 + B*H*q_pitch)
   void* dq;
   void* dk0;
   void* dv0;
@@ -135,6 +136,26 @@ struct Geo {
       a = 0;
       b = Tkv;
     }
+  }
+
+  // Position of local row `row` in the per-run, 64-aligned layout of qruns().
+  __host__ __device__ int prow(int row) const {
+    if (layout == LAYOUT_ZIGZAG) {
+      const int c = T / 2;
+      return row < c ? row : (c + 63) / 64 * 64 + (row - c);
+    }
+    return row;
+  }
+
+  // Inverse of prow: the local row at padded position p, or -1 for padding.
+  __host__ __device__ int trow(int p) const {
+    if (layout == LAYOUT_ZIGZAG) {
+      const int c = T / 2, c64 = (c + 63) / 64 * 64;
+      if (p < c) return p;
+      if (p < c64 || p - c64 >= c) return -1;
+      return c + (p - c64);
+    }
+    return p < T ? p : -1;
   }
 
   // Transposed-copy layout of the local query rows (one entry per run) and of
@@ -496,13 +517,18 @@ __device__ __forceinline__ f32x8 lds_col8(const float* tile, int stride, int k0,
 
 // ---- swizzled LDS tiles filled by direct global->LDS loads -----------------
 // A tile of rows of RB bytes is stored unpadded; the 16-byte chunk c of row r
-// sits in chunk slot c ^ sw(r), with sw(r) = (r mod 8) * U (U = chunks per MFMA
-// operand: 1 for bf16, 2 for fp32). Eight consecutive rows read at the same
-// chunk then hit eight different 16-byte bank groups, and an operand's U chunks
-// stay adjacent.
+// sits in chunk slot c ^ sw(r). sw is a multiple of U (16-byte chunks per MFMA
+// operand: 1 for bf16, 2 for fp32), so an operand's chunks stay adjacent. The
+// masks are the ones measured fastest on gfx950 for 16-byte reads of one
+// operand column by 32 consecutive rows (per wave, 4 waves per CU: 21.7 cycles
+// per read for 256-byte rows with r mod 16, against 32 with r mod 8; 17.3 for
+// 128-byte rows with r mod 8; 12.8 for 64-byte rows with (r / 2) mod 4).
 template <int RB, int U>
 __device__ __forceinline__ int sw_mask(int r) {
-  return ((r & 7) * U) & (RB / 16 - 1);
+  constexpr int CPR = RB / 16;
+  if constexpr (CPR >= 16) return ((r & 15) * U) & (CPR - 1);
+  else if constexpr (CPR == 8) return ((r & 7) * U) & 7;
+  else return (((r >> 1) & 3) * U) & (CPR - 1);
 }
 
 // LDS byte address of a pointer into __shared__ memory.
@@ -533,27 +559,46 @@ __device__ __forceinline__ void lds_dma16(const char* base, unsigned voff, unsig
       : "memory");
 }
 
-// Copy R rows of a tile into `lds` with global_load_lds_dwordx4 (no VGPR
+// Copy R rows of a tile to LDS byte address `lds` with global_load_lds_dwordx4 (no VGPR
 // staging): each wave instruction writes 1 KB of LDS, lane i at byte 16 i, so
 // lane i fetches the chunk that belongs in that slot. Row r of the tile is read
 // at `base` + r * `stride` bytes (base uniform, the per-lane part 32-bit); rows
 // at or past `nvalid` re-read row nvalid - 1. The copies complete
-// asynchronously (vmcnt). 4 waves per workgroup split the instructions.
-template <int R, int RB, int U>
-__device__ __forceinline__ void dma_tile(char* lds, const char* base, unsigned stride, int nvalid,
-                                         int w, int lane) {
-  constexpr int CPR = RB / 16;            // chunks per row
-  constexpr int RPI = 64 / CPR;           // rows per wave instruction
-  constexpr int NI = R / RPI / 4;         // instructions per wave
+// asynchronously (vmcnt). 4 waves per workgroup split the instructions; `w`
+// (the wave index) should be wave-uniform in a scalar register.
+template <int R, int RB>
+struct DmaShape {
+  static constexpr int CPR = RB / 16;     // chunks per row
+  static constexpr int RPI = 64 / CPR;    // rows per wave instruction
+  static constexpr int NI = R / RPI / 4;  // instructions per wave
   static_assert(NI >= 1 && NI * RPI * 4 == R, "tile does not split over 4 waves");
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int r0 = (w * NI + i) * RPI;
-    const int r = r0 + lane / CPR;
+};
+
+// Instruction i (0 <= i < NI) of this wave's share of the copy.
+template <int R, int RB, int U>
+__device__ __forceinline__ void dma_tile_part(unsigned lds, const char* base, unsigned stride,
+                                              int nvalid, int w, int lane, int i) {
+  using S = DmaShape<R, RB>;
+  const int r0 = (w * S::NI + i) * S::RPI;
+  const int rl = lane / S::CPR;
+  if (nvalid >= R) {
+    // Full tile: the row base is scalar, the lane part depends on r0 mod 16 only.
+    const unsigned off =
+        (unsigned)rl * stride + 16u * (unsigned)((lane % S::CPR) ^ sw_mask<RB, U>((r0 & 15) + rl));
+    lds_dma16(base + (long long)r0 * stride, off, lds + (unsigned)(r0 * RB));
+  } else {
+    const int r = r0 + rl;
     const int rr = r < nvalid ? r : nvalid - 1;
-    const unsigned off = (unsigned)rr * stride + 16u * (unsigned)((lane % CPR) ^ sw_mask<RB, U>(r));
-    lds_dma16(base, off, lds_addr(lds + r0 * RB));
+    const unsigned off = (unsigned)rr * stride + 16u * (unsigned)((lane % S::CPR) ^ sw_mask<RB, U>(r));
+    lds_dma16(base, off, lds + (unsigned)(r0 * RB));
   }
+}
+
+template <int R, int RB, int U>
+__device__ __forceinline__ void dma_tile(unsigned lds, const char* base, unsigned stride, int nvalid,
+                                         int w, int lane) {
+#pragma unroll
+  for (int i = 0; i < DmaShape<R, RB>::NI; ++i) dma_tile_part<R, RB, U>(lds, base, stride, nvalid, w, lane, i);
 }
 
 // MFMA operand of 8 consecutive elements (columns col..col+7) of row `row` of a

@@ -45,7 +45,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const Args a) {
   constexpr int BM = C::BM, BN = C::BN, KS = C::KS, DB = C::DB;
   __shared__ __attribute__((aligned(16))) char smem[C::LDS];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int BH = a.B * a.H;
   const int trank = blockIdx.x / BH, bh = blockIdx.x % BH, b = bh / a.H, h = bh % a.H;
   const Geo geo{a.layout, a.cp, a.rank, a.T, a.Tkv};
@@ -81,10 +82,13 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const Args a) {
   const float c2 = a.c2;
 
   // LDS: two K stages, then two V^T stages, swizzled, filled by direct loads.
+  // (pointers for the reads, LDS byte addresses for the copies)
   char* const kb0 = smem;
   char* const kb1 = kb0 + C::KBYTES;
   char* const vb0 = kb1 + C::KBYTES;
   char* const vb1 = vb0 + C::VBYTES;
+  const unsigned sbase = lds_addr(smem);
+  auto la = [&](const char* p) { return sbase + (unsigned)(p - smem); };
   const char* const kbase = reinterpret_cast<const char*>(k0b);
   const char* const vbase = reinterpret_cast<const char*>(vtb);
   const unsigned krow = (unsigned)(rs * (long long)sizeof(T));
@@ -92,11 +96,11 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const Args a) {
   // K rows past the end re-read the last row: those keys are masked.
   auto dma_k = [&](char* dst, int s0) {
     const int nv = a.Tkv - s0 < BN ? a.Tkv - s0 : BN;
-    dma_tile<BN, C::KRB, C::U>(dst, kbase + (long long)s0 * krow, krow, nv, w, lane);
+    dma_tile<BN, C::KRB, C::U>(la(dst), kbase + (long long)s0 * krow, krow, nv, w, lane);
   };
   // V^T rows are the D columns; the copy is zero padded to 64 positions.
   auto dma_v = [&](char* dst, int s0) {
-    dma_tile<D, C::VRB, C::U>(dst, vbase + (long long)s0 * (long long)sizeof(T), vrow, D, w, lane);
+    dma_tile<D, C::VRB, C::U>(la(dst), vbase + (long long)s0 * (long long)sizeof(T), vrow, D, w, lane);
   };
 
   // S^T = K Q^T for 64 keys: two 32-key accumulator chains, lane = query.
@@ -182,8 +186,21 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const Args a) {
 
   auto step = [&](f32x16 (&sc)[2], f32x16 (&sn)[2], const char* Kn, const char* Vc, char* Kw,
                   char* Vw) {
-    if (i2.valid) dma_k(Kw, i2.s0);
-    if (i1.valid) dma_v(Vw, i1.s0);
+    // Copies of K(j+2) and V^T(j+1), one instruction at a time between the
+    // phase A MFMAs (a missing tile re-copies the current one into the free
+    // stage, so the sequence has no branches).
+    constexpr int NKI = DmaShape<BN, C::KRB>::NI, NVI = DmaShape<D, C::VRB>::NI;
+    constexpr int NDMA = NKI + NVI;
+    const int dk0 = i2.valid ? i2.s0 : it.s0, dv0 = i1.valid ? i1.s0 : it.s0;
+    const int dnv = a.Tkv - dk0 < BN ? a.Tkv - dk0 : BN;
+    const unsigned lkw = la(Kw), lvw = la(Vw);
+    auto dma_part = [&](int k) {
+      if (k < NKI)
+        dma_tile_part<BN, C::KRB, C::U>(lkw, kbase + (long long)dk0 * krow, krow, dnv, w, lane, k);
+      else
+        dma_tile_part<D, C::VRB, C::U>(lvw, vbase + (long long)dv0 * (long long)sizeof(T), vrow, D, w,
+                                       lane, k - NKI);
+    };
     // Phase A: S^T(j+1) on MFMA (stale LDS when there is no tile j+1: the
     // result is then never used); P(j) and its row sum on VALU. The order is
     // fixed by scheduling fences: in step i the K operand of MFMA i+2 is read,
@@ -205,6 +222,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const Args a) {
         if (i + 2 < NQ)
           ka[(i + 2) % 3] = lds_sw8<T, C::KRB>(Kn, 32 * ((i + 2) & 1) + l32, 16 * ((i + 2) >> 1) + 8 * g);
         mfma16(ka[i % 3], qreg[i >> 1], sn[i & 1]);
+#pragma unroll
+        for (int k = (NDMA * i + NQ - 1) / NQ; k < (NDMA * (i + 1) + NQ - 1) / NQ; ++k) dma_part(k);
         // Exponentials: 32 per lane over the NQ steps.
 #pragma unroll
         for (int e = (32 * i) / NQ; e < (32 * (i + 1)) / NQ; ++e)

@@ -110,8 +110,10 @@ int eagle3_abi_version(void);
 /* Message for the last nonzero status returned on this thread ("" if none). */
 const char* eagle3_last_error(void);
 
-/* Bytes of device workspace eagle3_attn_bwd / eagle3_shard_bwd need: delta = rowsum(dO*O),
- * float32 [B, H, T]. 0 when T == 0. Returns 0 and sets the last error for an invalid
+/* Bytes of device workspace eagle3_attn_bwd / eagle3_shard_bwd need: delta = rowsum(dO*O)
+ * and lse*log2(e) (float32 [B, H, P]) and transposed copies of q and dout (dtype
+ * [B, H, D, P]), P = T with each local run (the two zig-zag chunks) padded to a multiple
+ * of 64 positions. 0 when T == 0. Returns 0 and sets the last error for an invalid
  * problem. */
 size_t eagle3_bwd_workspace_bytes(const e3_problem* p);
 
@@ -167,10 +169,11 @@ int lse_merge(float* out, float* lse, const float* block_out, const float* block
 /* ---- Measurement hook ---------------------------------------------------------------- */
 
 /* While `events` is non-NULL, every compute entry point called on this thread records
- * events[0] on its stream before its first kernel and events[k+1] after its k-th kernel
- * (at most `capacity` events; the forward launches 2 kernels: the V transpose and the
- * attention kernel; the backward 3: delta, dK/dV, dQ). The caller creates and owns the
- * events; NULL stops recording. Returns E3_OK. */
+ * events[0] on its stream before its first kernel and events[k+1] after its k-th stage
+ * (at most `capacity` events; the forward has 2 stages: the V transpose and the
+ * attention kernel; the backward 4: delta and lse*log2(e), the Q and dO transposes,
+ * dK/dV, dQ). The caller creates and owns the events; NULL stops recording. Returns
+ * E3_OK. */
 int eagle3_set_timing_events(hipEvent_t* events, int capacity);
 
 /* Number of events recorded by the last compute entry point called on this thread. */

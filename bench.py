@@ -28,7 +28,7 @@ if ROOT not in sys.path:
 METRIC = "EAGLE-3 mixed attn fwd+bwd TFLOP/s (causal) + % bf16 MFMA peak, T=4096 H=32 D=128"
 PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}   # MI355X dense MFMA (bf16) / fp32 vector
 PEAK_GBS = 8000.0                               # MI355X HBM3E
-KERNELS = ["xpose_v", "fwd", "delta", "xpose_qdo", "dkdv", "dq"]
+KERNELS = ["xpose_v", "fwd", "delta", "xpose_k", "dq", "dkdv", "diag_tail"]
 
 
 def log(msg):
@@ -52,12 +52,18 @@ def kernel_work(w, P0):
         "fwd": dict(flop=4 * pf, diag_flop=4 * diagf, bytes=u + 2 * ukv + 2 * N * u + u + rowf),
         # dO, O, lse read; delta and lse*log2(e) written
         "delta": dict(flop=0, diag_flop=0, bytes=2 * u + 3 * rowf),
-        # q and dO read, their transposed copies written
-        "xpose_qdo": dict(flop=0, diag_flop=0, bytes=4 * u),
+        # k0 read, its transposed copy written (the q and dO transposes run on the
+        # side stream during dq and are not in any stage)
+        "xpose_k": dict(flop=0, diag_flop=0, bytes=2 * ukv),
         # q, dO, k0, v0, lse, delta read; dk0, dv0 written; S, dP, dV, dK = 4 GEMMs
+        # (the diagonal-gradient kernel runs alongside on the side stream)
         "dkdv": dict(flop=8 * pf, diag_flop=0, bytes=2 * u + 4 * ukv + 2 * rowf),
-        # q, dO, k0, v0, lse, delta, kd, vd read; dq, dkd, dvd written; S, dP, dQ = 3 GEMMs
-        "dq": dict(flop=6 * pf, diag_flop=10 * diagf, bytes=3 * u + 2 * ukv + 4 * N * u + 2 * rowf),
+        # q, dO, k0, v0, lse, delta read; dq (or its float32 partial) written;
+        # S, dP, dQ = 3 GEMMs
+        "dq": dict(flop=6 * pf, diag_flop=0, bytes=3 * u + 2 * ukv + 2 * rowf),
+        # wait for the diagonal gradients: q, dO, kd, vd, dq partial read;
+        # dq, dkd, dvd written (the part of that kernel not hidden under dK/dV)
+        "diag_tail": dict(flop=0, diag_flop=10 * diagf, bytes=2 * u + 4 * N * u + 3 * u),
     }
 
 
@@ -199,7 +205,7 @@ def main():
     log(f"[bench] {args.steps} steps: {total_ms:.3f} ms ({ms_per_step:.4f} ms/step, wall {wall_ms:.1f} ms)")
 
     # (2) per-kernel times: events recorded by the library around each kernel
-    nfwd, nbwd = 3, 5
+    nfwd, nbwd = 3, 6
     per = {k: [] for k in KERNELS}
     fwd_ms, bwd_ms, flushed = [], [], []
     flush_buf = None if args.no_flush else torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -224,12 +230,10 @@ def main():
         b0 = r * nbwd
         per["xpose_v"].append(ev.elapsed_ms(evf[f0], evf[f0 + 1]))
         per["fwd"].append(ev.elapsed_ms(evf[f0 + 1], evf[f0 + 2]))
-        per["delta"].append(ev.elapsed_ms(evb[b0], evb[b0 + 1]))
-        per["xpose_qdo"].append(ev.elapsed_ms(evb[b0 + 1], evb[b0 + 2]))
-        per["dkdv"].append(ev.elapsed_ms(evb[b0 + 2], evb[b0 + 3]))
-        per["dq"].append(ev.elapsed_ms(evb[b0 + 3], evb[b0 + 4]))
+        for i, k in enumerate(["delta", "xpose_k", "dq", "dkdv", "diag_tail"]):
+            per[k].append(ev.elapsed_ms(evb[b0 + i], evb[b0 + i + 1]))
         fwd_ms.append(ev.elapsed_ms(evf[f0], evf[f0 + 2]))
-        bwd_ms.append(ev.elapsed_ms(evb[b0], evb[b0 + 4]))
+        bwd_ms.append(ev.elapsed_ms(evb[b0], evb[b0 + 5]))
         flushed.append(fwd_ms[-1] + bwd_ms[-1])
     ev.destroy(se)
     ev.destroy(evf)

@@ -9,6 +9,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <map>
 #include <string>
 
 #include "e3_common.h"
@@ -185,8 +186,8 @@ int fwd_impl(const e3_problem* p, const void* q, const void* k0, const void* v0,
 }
 
 struct BwdWs {
-  int pitch;
-  size_t delta, qt, dot, total;
+  int pitch, kv_pitch;
+  size_t delta, qt, dot, kt, dqd, total;
 };
 
 BwdWs bwd_ws_layout(const e3_problem* p) {
@@ -197,7 +198,11 @@ BwdWs bwd_ws_layout(const e3_problem* p) {
   l.delta = rows * sizeof(float);
   l.qt = 2 * rows * sizeof(float);
   l.dot = l.qt + rows * p->D * esz;
-  l.total = l.dot + rows * p->D * esz;
+  l.kt = l.dot + rows * p->D * esz;
+  l.kv_pitch = geo_of(p).kvruns().pitch;
+  l.dqd = l.kt + (((size_t)p->B * p->H * p->D * l.kv_pitch * esz + 255) & ~(size_t)255);
+  const int N = p->num_blocks - 1;
+  l.total = l.dqd + (N > 0 ? (size_t)p->B * p->T * p->H * p->D * sizeof(float) : 0);
   return l;
 }
 
@@ -230,7 +235,9 @@ int bwd_impl(const e3_problem* p, const void* dout, const void* q, const void* k
   a.lse_in = lse;
   {
     // workspace: lse2, delta (float [B,H,P]), then Q^T and dO^T (dtype [B,H,D,P]),
-    // P = the 64-aligned per-run row layout of the local queries.
+    // P = the 64-aligned per-run row layout of the local queries; then K^T (dtype
+    // [B,H,D,P_kv], P_kv = T_kv rounded up to 64) and the diagonal part of dq
+    // (float [B,T,H,D], when there are diagonal blocks).
     const BwdWs l = bwd_ws_layout(p);
     char* w = static_cast<char*>(ws);
     a.q_pitch = l.pitch;
@@ -238,6 +245,9 @@ int bwd_impl(const e3_problem* p, const void* dout, const void* q, const void* k
     a.delta = reinterpret_cast<float*>(w + l.delta);
     a.qt = w + l.qt;
     a.dot = w + l.dot;
+    a.kt = w + l.kt;
+    a.kv_pitch = l.kv_pitch;
+    a.dqd = reinterpret_cast<float*>(w + l.dqd);
   }
   a.dq = dq;
   a.dk0 = dk0;
@@ -254,6 +264,48 @@ int doc_lo_host(const e3_problem* p, int pos) {
 }
 
 }  // namespace
+
+namespace {
+struct SideRes {
+  hipStream_t s = nullptr;
+  hipEvent_t fork[2] = {nullptr, nullptr}, join[2] = {nullptr, nullptr};
+};
+thread_local std::map<int, SideRes> t_side;
+
+hipError_t side_res(SideRes*& out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  SideRes& r = t_side[dev];
+  if (!r.s) {
+    if ((e = hipStreamCreateWithFlags(&r.s, hipStreamNonBlocking)) != hipSuccess) return e;
+    for (int k = 0; k < 2; ++k) {
+      if ((e = hipEventCreateWithFlags(&r.fork[k], hipEventDisableTiming)) != hipSuccess) return e;
+      if ((e = hipEventCreateWithFlags(&r.join[k], hipEventDisableTiming)) != hipSuccess) return e;
+    }
+  }
+  out = &r;
+  return hipSuccess;
+}
+}  // namespace
+
+hipError_t e3::side_begin(hipStream_t main, int k, hipStream_t& side) {
+  SideRes* r = nullptr;
+  hipError_t e = side_res(r);
+  if (e != hipSuccess) return e;
+  if ((e = hipEventRecord(r->fork[k], main)) != hipSuccess) return e;
+  if ((e = hipStreamWaitEvent(r->s, r->fork[k], 0)) != hipSuccess) return e;
+  side = r->s;
+  return hipSuccess;
+}
+
+hipError_t e3::side_end(hipStream_t main, int k) {
+  SideRes* r = nullptr;
+  hipError_t e = side_res(r);
+  if (e != hipSuccess) return e;
+  if ((e = hipEventRecord(r->join[k], r->s)) != hipSuccess) return e;
+  return hipStreamWaitEvent(main, r->join[k], 0);
+}
 
 void e3::timing_mark(hipStream_t st) {
   if (g_events && g_events_n < g_events_cap) (void)hipEventRecord(g_events[g_events_n++], st);

@@ -9,19 +9,24 @@
 // Kernels, no atomics (every output element has one writer):
 //   delta_kernel  delta[b,h,t] = <dO_t, O_t> (O = the stored merged out) and
 //                 lse2 = lse * log2(e), in the 64-aligned per-run row layout
-//   xpose (x2)    Q^T and dO^T copies (e3_xpose.hip) for the dK/dV operands
-//   dkdv_kernel   one workgroup per 128 block-0 keys (32 per wave, lane = key);
-//                 loops over the query tiles that see them:
+//   xpose (x3)    Q^T and dO^T copies (e3_xpose.hip) for the dK/dV operands
+//                 (side stream, overlapping dQ) and the K^T copy for dQ
+//   dkdv_kernel   one workgroup per 128 block-0 keys (lane = key); loops over
+//                 the query tiles that see them:
 //                   S = Q K^T, P, dP = dO V^T, dS = P (dP - delta),
 //                   dV += P^T dO, dK += scale dS^T Q
 //                 Q / dO tiles and their transposes stream through swizzled
-//                 LDS stages filled by direct global->LDS copies; the S / dP
-//                 MFMAs of tile j+1 overlap the P / dS arithmetic of tile j.
+//                 LDS stages filled by direct global->LDS copies; one wave of
+//                 each pair forms P and dV, the other dP, dS and dK, so the two
+//                 waves sharing a SIMD overlap their MFMA and VALU phases.
+//   diag_bwd_kernel  (side stream, after dQ, overlapping dK/dV) the closed-form
+//                 diagonal terms pi = exp(y - lse), dpi = <dO, vd>,
+//                 ds = pi (dpi - delta): dkd = scale ds q, dvd = pi dO, and
+//                 dq = (float32 partial from dQ) + scale sum_i ds_i kd_i
 //   dq_kernel     one workgroup per 128 query rows (lane = query, as in the
-//                 forward); loops over the visible key tiles in ring order:
-//                   dQ += dS K; then the epilogue adds the diagonal terms
-//                   pi = exp(y - lse), dpi = <dO, vd>, ds = pi (dpi - delta),
-//                   dq += scale ds kd, dkd = scale ds q, dvd = pi dO.
+//                 forward); loops over the visible 32-key tiles in ring order
+//                 (K, V and K^T staged in swizzled LDS by direct copies):
+//                   dQ += dS K (float32 partial when there are diagonals).
 #include "e3_common.h"
 
 namespace e3 {
@@ -64,8 +69,10 @@ __global__ __launch_bounds__(256) void delta_kernel(const Args a) {
 // ---------------------------------------------------------------------------
 template <typename T, int D>
 struct DkdvCfg {
-  static constexpr int BNK = 128;            // keys per workgroup (32 per wave)
-  static constexpr int BMQ = 32;            // queries per step
+  static constexpr int NT = 512;             // 8 waves: 4 that form P, 4 that form dS
+  static constexpr int NW = NT / 64;
+  static constexpr int BNK = 128;            // keys per workgroup (32 per wave of each kind)
+  static constexpr int BMQ = sizeof(T) == 2 ? 64 : 32;   // queries per step
   static constexpr int MB = BMQ / 32;        // 32-query blocks per step
   static constexpr int KS = D / 16;
   static constexpr int DB = D / 32;
@@ -73,12 +80,10 @@ struct DkdvCfg {
   static constexpr int RRB = D * (int)sizeof(T);        // row tiles Q, dO [BMQ][D]: row bytes
   static constexpr int CRB = BMQ * (int)sizeof(T);      // column tiles Q^T, dO^T [D][BMQ]
   static constexpr int RT = BMQ * RRB, CT = D * CRB;     // bytes per tile
-  static constexpr int RSTAGE = 2 * RT;                 // Q, dO
-  static constexpr int CSTAGE = 2 * CT;                 // Q^T, dO^T
+  static constexpr int STAGE = 2 * RT + 2 * CT;         // Q, dO, Q^T, dO^T
   static constexpr int LSTAGE = 2 * BMQ * 4;            // lse2, delta
-  // The tile stages come first so that every operand read addresses them with
-  // one lane register and an immediate offset (below 64 KB).
-  static constexpr int LDS = 2 * RSTAGE + 2 * CSTAGE + 2 * LSTAGE;
+  static constexpr int PW = 64 * 16 * MB * (int)sizeof(T);   // P of one wave (per lane: 16 MB values)
+  static constexpr int LDS = 2 * STAGE + 2 * LSTAGE + 4 * PW;
 };
 
 // Query tiles (rows of the share) that can see keys [k_lo, k_hi) with document
@@ -120,26 +125,29 @@ struct QIter {
   __device__ int gpos0() const { return gb + t0; }
 };
 
+// Waves 0-3 ("P" waves) hold K for their 32 keys and form S = Q K^T, P and
+// dV += dO^T P; waves 4-7 ("dS" waves) hold V for the same keys and form
+// dP = dO V^T, dS = P (dP - delta) and dK += Q^T dS, taking P from the P wave of
+// their keys through LDS. Wave w and w + 4 share a SIMD, so the exponentials of
+// one overlap the MFMAs of the other. Both kinds run the same MFMA code on
+// different tiles (rows Q or dO, columns dO^T or Q^T) and share registers.
 template <typename T, int D>
-__global__ __launch_bounds__(256, 1) void dkdv_kernel(const Args a) {
+__global__ __launch_bounds__(512, 1) void dkdv_kernel(const Args a) {
   using C = DkdvCfg<T, D>;
   using Op = typename V8<T>::type;
-  constexpr int BNK = C::BNK, BMQ = C::BMQ, MB = C::MB, KS = C::KS, DB = C::DB;
+  constexpr int BNK = C::BNK, BMQ = C::BMQ, MB = C::MB, KS = C::KS, DB = C::DB, NW = C::NW;
   constexpr int sz = (int)sizeof(T);
   __shared__ __attribute__((aligned(16))) char smem[C::LDS];
-  // Row stages hold Q at 0 and dO at RT; column stages hold Q^T at 0 and dO^T
-  // at CT; each column stage has an lse2 / delta stage (BMQ floats each).
-  char* const rb0 = smem;
-  char* const rb1 = rb0 + C::RSTAGE;
-  char* const cb0 = rb1 + C::RSTAGE;
-  char* const cb1 = cb0 + C::CSTAGE;
-  char* const lb0 = cb1 + C::CSTAGE;
-  auto lstage = [&](const char* cb) { return lb0 + (cb == cb0 ? 0 : C::LSTAGE); };
+  // Stage p: Q at 0, dO at RT, Q^T at 2 RT, dO^T at 2 RT + CT. Then the two
+  // lse2 / delta stages and the P exchange buffers.
+  char* const lb0 = smem + 2 * C::STAGE;
+  char* const pbuf = lb0 + 2 * C::LSTAGE;
   const unsigned sbase = lds_addr(smem);
-  auto la = [&](const char* p) { return sbase + (unsigned)(p - smem); };
 
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int role = w >> 2;   // 0: S, P, dV   1: dP, dS, dK
+  const int kw = w & 3;      // 32-key block
   const int BH = a.B * a.H;
   const int kt = tile_order(blockIdx.x / BH, (a.Tkv + BNK - 1) / BNK), bh = blockIdx.x % BH,
             b = bh / a.H, h = bh % a.H;
@@ -148,8 +156,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const Args a) {
   const int kt1 = (kt0 + BNK) < a.Tkv ? (kt0 + BNK) : a.Tkv;
 
   const long long rs = (long long)a.H * D;
-  const T* k0b = reinterpret_cast<const T*>(a.k0) + (long long)b * a.k0_bs + (long long)h * D;
-  const T* v0b = reinterpret_cast<const T*>(a.v0) + (long long)b * a.k0_bs + (long long)h * D;
+  const T* kvb = reinterpret_cast<const T*>(role ? a.v0 : a.k0) + (long long)b * a.k0_bs + (long long)h * D;
   const char* const qbytes =
       reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.q) + (long long)b * a.T * rs + (long long)h * D);
   const char* const obytes =
@@ -162,58 +169,36 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const Args a) {
   const unsigned rrow = (unsigned)(rs * sz), crow = (unsigned)((long long)a.q_pitch * sz);
 
   // This lane's key; a query at global position gm sees it iff s <= gm < s_hi.
-  const int s = kt0 + w * 32 + l32;
+  const int s = kt0 + kw * 32 + l32;
   const bool svalid = s < a.Tkv;
   const int s_hi = svalid ? doc_hi_of(a.cu, a.ndocs, s, a.Tkv) : 0;
-  Op kreg[KS], vreg[KS];
+  Op kv[KS];   // K (P waves) or V (dS waves) of this lane's key
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    kreg[ks] = svalid ? load8(k0b + (long long)s * rs + 16 * ks + 8 * g) : zero8<T>();
-    vreg[ks] = svalid ? load8(v0b + (long long)s * rs + 16 * ks + 8 * g) : zero8<T>();
-  }
+  for (int ks = 0; ks < KS; ++ks)
+    kv[ks] = svalid ? load8(kvb + (long long)s * rs + 16 * ks + 8 * g) : zero8<T>();
   const int hi_min = doc_hi_of(a.cu, a.ndocs, kt0, a.Tkv);   // smallest document end of the tile
   const int q_hi = doc_hi_of(a.cu, a.ndocs, kt1 - 1, a.Tkv);  // queries past this see no key
 
-  f32x16 dk[DB], dv[DB];
+  f32x16 acc[DB];   // dV^T (P waves) or dK^T (dS waves)
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      dk[db][j] = 0.f;
-      dv[db][j] = 0.f;
-    }
+    for (int j = 0; j < 16; ++j) acc[db][j] = 0.f;
   const float c2 = a.c2;
 
-  auto dma_rows = [&](char* dst, const QIter& q) {
-    const int r0 = q.row0(), nr = q.nrows(BMQ);
-    dma_tile<BMQ, C::RRB, C::U>(la(dst), qbytes + (long long)r0 * rrow, rrow, nr, w, lane);
-    dma_tile<BMQ, C::RRB, C::U>(la(dst) + C::RT, obytes + (long long)r0 * rrow, rrow, nr, w, lane);
-  };
-  auto dma_cols = [&](char* dst, const QIter& q) {
-    const int p0 = geo.prow(q.row0());
-    dma_tile<D, C::CRB, C::U>(la(dst), qtbytes + (long long)p0 * sz, crow, D, w, lane);
-    dma_tile<D, C::CRB, C::U>(la(dst) + C::CT, otbytes + (long long)p0 * sz, crow, D, w, lane);
+  // Copy one query tile (rows, columns, lse2 / delta) into stage p; the 8
+  // waves share the instructions.
+  auto dma_stage = [&](int p, const QIter& q) {
+    const unsigned st = sbase + (unsigned)(p * C::STAGE);
+    const int r0 = q.row0(), nr = q.nrows(BMQ), p0 = geo.prow(r0);
+    dma_tile<BMQ, C::RRB, C::U, NW>(st, qbytes + (long long)r0 * rrow, rrow, nr, w, lane);
+    dma_tile<BMQ, C::RRB, C::U, NW>(st + C::RT, obytes + (long long)r0 * rrow, rrow, nr, w, lane);
+    dma_tile<D, C::CRB, C::U, NW>(st + 2 * C::RT, qtbytes + (long long)p0 * sz, crow, D, w, lane);
+    dma_tile<D, C::CRB, C::U, NW>(st + 2 * C::RT + C::CT, otbytes + (long long)p0 * sz, crow, D, w, lane);
     if (w == 0 && lane < BMQ / 2) {
       const unsigned voff = lane < BMQ / 4 ? 16u * lane : ldoff + 16u * (lane - BMQ / 4);
-      lds_dma16(lbytes + (long long)p0 * 4, voff, la(lstage(dst)));
+      lds_dma16(lbytes + (long long)p0 * 4, voff, sbase + (unsigned)(lb0 - smem) + p * C::LSTAGE);
     }
-  };
-  // S^T-like scores and dP for a row stage: lane = key, 16 queries per block.
-  auto sdp = [&](const char* R, f32x16 (&sp)[MB], f32x16 (&dp)[MB]) {
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        sp[mb][j] = 0.f;
-        dp[mb][j] = 0.f;
-      }
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        mfma16(lds_sw8<T, C::RRB>(R, 32 * mb + l32, 16 * ks + 8 * g), kreg[ks], sp[mb]);
-        mfma16(lds_sw8<T, C::RRB>(R + C::RT, 32 * mb + l32, 16 * ks + 8 * g), vreg[ks], dp[mb]);
-      }
   };
   auto interior = [&](const QIter& q) {
     const int gq0 = q.gpos0();
@@ -221,7 +206,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const Args a) {
            gq0 + BMQ - 1 < hi_min;
   };
   // Query m of the tile (m = 4g + o, o = 32mb + 8(j/4) + j%4 a constant per
-  // element) sees this lane's key when mlo <= m <= mhi.
+  // element) sees this lane's key when lo <= m - 4g <= hi.
   auto mask = [&](f32x16 (&sp)[MB], const QIter& q) {
     const int gq0 = q.gpos0(), nr = q.nrows(BMQ);
     const int lo = s - gq0 - 4 * g;
@@ -235,176 +220,97 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const Args a) {
       }
   };
 
-  QIter it, i1, i2;
+  QIter it, i1;
   it.begin(geo, kt0, q_hi, BMQ);
   i1 = it;
   if (i1.valid) i1.next(geo, BMQ);
-  i2 = i1;
-  if (i2.valid) i2.next(geo, BMQ);
-  if (it.valid) {
-    dma_rows(rb0, it);
-    dma_cols(cb0, it);
-  }
-  if (i1.valid) dma_rows(rb1, i1);
+  if (it.valid) dma_stage(0, it);
   wait_all();
   __syncthreads();
-  f32x16 sa[MB], da[MB], sb[MB], dbb[MB];
-  if (it.valid) sdp(rb0, sa, da);
-  __syncthreads();   // the first step overwrites row stage 0
 
-  // Step j: S(j), dP(j) in registers; rows of tile j+1 and columns of tile j in
-  // LDS. Starts the copies of rows(j+2) and columns(j+1) into the stages step
-  // j-1 finished with. Phase A: S, dP of tile j+1 on MFMA while P(j), dS(j) are
-  // formed on VALU; phase B: dV += dO^T P, dK += Q^T dS for tile j.
-  auto step = [&](f32x16 (&sc)[MB], f32x16 (&dc)[MB], f32x16 (&sn)[MB], f32x16 (&dn)[MB],
-                  const char* Rn, const char* Cc, char* Rw, char* Cw) {
-    // Copies of rows(j+2) and columns(j+1), one instruction at a time between
-    // the phase A MFMAs (a missing tile re-copies the current one into the free
-    // stage, so the sequence has no branches).
-    constexpr int NR = DmaShape<BMQ, C::RRB>::NI, NC = DmaShape<D, C::CRB>::NI;
-    constexpr int NDMA = 2 * NR + 2 * NC + 1;
-    const int dr0 = (i2.valid ? i2 : it).row0(), dnr = (i2.valid ? i2 : it).nrows(BMQ);
-    const int dp0 = geo.prow((i1.valid ? i1 : it).row0());
-    const unsigned lrw = la(Rw), lcw = la(Cw);
-    auto dma_part = [&](int k) {
-      if (k < NR) {
-        dma_tile_part<BMQ, C::RRB, C::U>(lrw, qbytes + (long long)dr0 * rrow, rrow, dnr, w, lane, k);
-      } else if (k < 2 * NR) {
-        dma_tile_part<BMQ, C::RRB, C::U>(lrw + C::RT, obytes + (long long)dr0 * rrow, rrow, dnr, w, lane, k - NR);
-      } else if (k < 2 * NR + NC) {
-        dma_tile_part<D, C::CRB, C::U>(lcw, qtbytes + (long long)dp0 * sz, crow, D, w, lane, k - 2 * NR);
-      } else if (k < 2 * NR + 2 * NC) {
-        dma_tile_part<D, C::CRB, C::U>(lcw + C::CT, otbytes + (long long)dp0 * sz, crow, D, w, lane,
-                                       k - 2 * NR - NC);
-      } else if (w == 0 && lane < BMQ / 2) {
-        const unsigned voff = lane < BMQ / 4 ? 16u * lane : ldoff + 16u * (lane - BMQ / 4);
-        lds_dma16(lbytes + (long long)dp0 * 4, voff, la(lstage(Cw)));
-      }
-    };
-    if (!interior(it)) mask(sc, it);
-    const float* L2s = reinterpret_cast<const float*>(lstage(Cc));
-    const float* Ds = L2s + BMQ;
-    // lse2 / delta of the tile's queries, 4 at a time (group e/4 of the lane's
-    // elements), read one group ahead.
-    auto ld4 = [&](int grp, f32x4& l, f32x4& d) {
-      const int off = 32 * (grp >> 2) + 8 * (grp & 3) + 4 * g;
-      l = *reinterpret_cast<const f32x4*>(L2s + off);
-      d = *reinterpret_cast<const f32x4*>(Ds + off);
-    };
-    // Phase A. MFMA i: ks = i / (2 MB), block mb, S (even) or dP (odd); its
-    // A operand is read two MFMAs ahead. E elements of P / dS per lane spread
-    // over the NQ steps.
-    Op pb[BMQ / 16], sbo[BMQ / 16];
+  char* const pw = pbuf + kw * C::PW;   // P of this key block, lane-major
+  for (int par = 0; it.valid; par ^= 1) {
+    const int cur = __builtin_amdgcn_readfirstlane(par);
+    const char* const st = smem + cur * C::STAGE;
+    const float* const L2s = reinterpret_cast<const float*>(lb0 + cur * C::LSTAGE);
+    const float* const Ds = L2s + BMQ;
+    if (i1.valid) dma_stage(cur ^ 1, i1);
+    // S^T (P waves, rows Q) or dP^T (dS waves, rows dO): lane = key.
+    f32x16 sp[MB];
     {
+      const char* const R = st + role * C::RT;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          sn[mb][j] = 0.f;
-          dn[mb][j] = 0.f;
-        }
-      constexpr int NQ = 2 * MB * KS, E = 16 * MB;
-      auto opnd = [&](int i) {
-        const int ks = i / (2 * MB), mb = (i / 2) % MB;
-        return lds_sw8<T, C::RRB>(Rn + (i & 1) * C::RT, 32 * mb + l32, 16 * ks + 8 * g);
-      };
-      Op ka[3];
-      ka[0] = opnd(0);
-      ka[1] = opnd(1);
-      f32x4 lg[2], dg[2];
-      ld4(0, lg[0], dg[0]);
+        for (int j = 0; j < 16; ++j) sp[mb][j] = 0.f;
 #pragma unroll
-      for (int i = 0; i < NQ; ++i) {
-        if (i + 2 < NQ) ka[(i + 2) % 3] = opnd(i + 2);
-        {
-          const int ks = i / (2 * MB), mb = (i / 2) % MB;
-          if (i & 1) mfma16(ka[i % 3], vreg[ks], dn[mb]);
-          else mfma16(ka[i % 3], kreg[ks], sn[mb]);
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+          mfma16(lds_sw8<T, C::RRB>(R, 32 * mb + l32, 16 * ks + 8 * g), kv[ks], sp[mb]);
+    }
+    Op ops[BMQ / 16];
+    if (role == 0) {
+      if (!interior(it)) mask(sp, it);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(L2s + 32 * mb + 8 * jj + 4 * g);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sp[mb][4 * jj + i] = fast_exp2(fmaf(sp[mb][4 * jj + i], c2, -l4[i]));
         }
 #pragma unroll
-        for (int k = (NDMA * i + NQ - 1) / NQ; k < (NDMA * (i + 1) + NQ - 1) / NQ; ++k) dma_part(k);
-#pragma unroll
-        for (int e = (E * i) / NQ; e < (E * (i + 1)) / NQ; ++e) {
-          const int mb = e >> 4, j = e & 15, grp = e >> 2;
-          if ((e & 3) == 0 && grp + 1 < E / 4) ld4(grp + 1, lg[(grp + 1) & 1], dg[(grp + 1) & 1]);
-          const float p = fast_exp2(fmaf(sc[mb][j], c2, -lg[grp & 1][j & 3]));
-          sc[mb][j] = p;
-          dc[mb][j] = p * (dc[mb][j] - dg[grp & 1][j & 3]);
-        }
-#pragma unroll
-        for (int q = 0; q < BMQ / 16; ++q)
-          if ((E * (i + 1)) / NQ >= 8 * (q + 1) && (E * i) / NQ < 8 * (q + 1)) {
-            pb[q] = to_op(sc[q >> 1], 8 * (q & 1), T());
-            sbo[q] = to_op(dc[q >> 1], 8 * (q & 1), T());
-            pin(pb[q]);
-            pin(sbo[q]);
-          }
-        __builtin_amdgcn_sched_barrier(0);
+      for (int q = 0; q < BMQ / 16; ++q) {
+        ops[q] = to_op(sp[q >> 1], 8 * (q & 1), T());
+        *reinterpret_cast<Op*>(pw + (q * 64 + lane) * (int)sizeof(Op)) = ops[q];
       }
     }
-    // Phase B: dV^T += dO^T P^T and dK^T += Q^T dS^T over the BMQ queries.
-    // Step k = (ks, db) issues the two MFMAs of one 32-row block of D; its
-    // operands are read two steps ahead.
+    __syncthreads();   // P of the tile is in LDS
+    if (role == 1) {
+#pragma unroll
+      for (int q = 0; q < BMQ / 16; ++q) {
+        const Op pq = *reinterpret_cast<const Op*>(pw + (q * 64 + lane) * (int)sizeof(Op));
+        const int mb = q >> 1, j0 = 8 * (q & 1);
+        const f32x4 d0 = *reinterpret_cast<const f32x4*>(Ds + 32 * mb + 8 * (j0 >> 2) + 4 * g);
+        const f32x4 d1 = *reinterpret_cast<const f32x4*>(Ds + 32 * mb + 8 * ((j0 >> 2) + 1) + 4 * g);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float dl = e < 4 ? d0[e] : d1[e - 4];
+          sp[mb][j0 + e] = (float)pq[e] * (sp[mb][j0 + e] - dl);
+        }
+        ops[q] = to_op(sp[mb], j0, T());
+      }
+    }
+    // dV^T += dO^T P^T (P waves) or dK^T += Q^T dS^T (dS waves).
     {
-      constexpr int NK = (BMQ / 16) * DB;
-      auto vop = [&](int k) {
-        return lds_sw8<T, C::CRB>(Cc + C::CT, 32 * (k % DB) + l32, 16 * (k / DB) + 8 * g);
-      };
-      auto qop = [&](int k) {
-        return lds_sw8<T, C::CRB>(Cc, 32 * (k % DB) + l32, 16 * (k / DB) + 8 * g);
-      };
-      Op va[3], qa[3];
-      va[0] = vop(0);
-      qa[0] = qop(0);
-      va[1] = vop(1);
-      qa[1] = qop(1);
+      const char* const Cc = st + 2 * C::RT + (1 - role) * C::CT;
 #pragma unroll
-      for (int k = 0; k < NK; ++k) {
-        if (k + 2 < NK) {
-          va[(k + 2) % 3] = vop(k + 2);
-          qa[(k + 2) % 3] = qop(k + 2);
-        }
-        mfma16(va[k % 3], pb[k / DB], dv[k % DB]);
-        mfma16(qa[k % 3], sbo[k / DB], dk[k % DB]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-    // The next tile's S / dP become the current ones (accumulator -> VALU registers).
+      for (int ks = 0; ks < BMQ / 16; ++ks)
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      sc[mb] = sn[mb];
-      dc[mb] = dn[mb];
+        for (int db = 0; db < DB; ++db)
+          mfma16(lds_sw8<T, C::CRB>(Cc, 32 * db + l32, 16 * ks + 8 * g), ops[ks], acc[db]);
     }
     it = i1;
-    i1 = i2;
-    if (i2.valid) i2.next(geo, BMQ);
+    if (i1.valid) i1.next(geo, BMQ);
     wait_all();
-    __syncthreads();
-  };
-  // One step per iteration; the stages alternate with the step parity.
-  for (int par = 0; it.valid; par ^= 1) {
-    const int odd = __builtin_amdgcn_readfirstlane(par);
-    step(sa, da, sb, dbb, odd ? rb0 : rb1, odd ? cb1 : cb0, odd ? rb1 : rb0, odd ? cb0 : cb1);
+    __syncthreads();   // the next stage is in LDS; this stage and P are free
   }
 
-  // Write dK0 = scale * dK, dV0 (rows of keys no query sees are zeros).
+  // dV0 (P waves) or dK0 = scale * dK (dS waves); keys no query sees get zeros.
   if (svalid) {
-    T* dkb = reinterpret_cast<T*>(a.dk0) + (long long)b * a.k0_bs + (long long)h * D + (long long)s * rs;
-    T* dvb = reinterpret_cast<T*>(a.dv0) + (long long)b * a.k0_bs + (long long)h * D + (long long)s * rs;
+    const float f = role ? a.scale : 1.f;
+    T* ob = reinterpret_cast<T*>(role ? a.dk0 : a.dv0) + (long long)b * a.k0_bs + (long long)h * D +
+            (long long)s * rs;
     typedef typename VecE<T, 4>::type v4;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        v4 x, y;
+        v4 x;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          x[i] = (T)(dk[db][4 * jj + i] * a.scale);
-          y[i] = (T)dv[db][4 * jj + i];
-        }
-        const int d0 = 32 * db + 8 * jj + 4 * g;
-        *reinterpret_cast<v4*>(dkb + d0) = x;
-        *reinterpret_cast<v4*>(dvb + d0) = y;
+        for (int i = 0; i < 4; ++i) x[i] = (T)(acc[db][4 * jj + i] * f);
+        *reinterpret_cast<v4*>(ob + 32 * db + 8 * jj + 4 * g) = x;
       }
   }
 }
@@ -414,34 +320,33 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const Args a) {
 // ---------------------------------------------------------------------------
 template <typename T, int D>
 struct DqCfg {
-  static constexpr int BM = 128;
-  static constexpr int BN = 64;
-  static constexpr int KSTR = Stride<T, D>::both;  // K is read both ways
-  static constexpr int VSTR = Stride<T, D>::nat;
-  static constexpr int OSTR = D + 4;
+  static constexpr int BM = 128;        // query rows per workgroup (32 per wave)
+  static constexpr int BN = 32;         // keys per step
   static constexpr int KS = D / 16;
   static constexpr int DB = D / 32;
-  static constexpr int STAGE = (BN * KSTR + BN * VSTR) * (int)sizeof(T);
+  static constexpr int U = 8 * (int)sizeof(T) / 16;    // 16-byte chunks per operand
+  static constexpr int KRB = D * (int)sizeof(T);       // K, V rows [BN][D]: row bytes
+  static constexpr int TRB = BN * (int)sizeof(T);      // K^T [D][BN]: row bytes
+  static constexpr int KT = BN * KRB, TT = D * TRB;    // bytes per tile
+  static constexpr int STAGE = 2 * KT + TT;            // K, V, K^T
+  static constexpr int OSTR = D + 4;
   static constexpr int LDS_KV = 2 * STAGE;
   static constexpr int LDS_EPI = 4 * 32 * OSTR * 4;
   static constexpr int LDS = LDS_KV > LDS_EPI ? LDS_KV : LDS_EPI;
   static constexpr int NB = sizeof(T) == 2 ? 8 : 2;   // diagonal blocks per epilogue group
 };
 
-#ifndef E3_DQ_OCC
-#define E3_DQ_OCC 2
-#endif
-
 template <typename T, int D>
-__global__ __launch_bounds__(256, E3_DQ_OCC) void dq_kernel(const Args a) {
+__global__ __launch_bounds__(256, 2) void dq_kernel(const Args a) {
   using C = DqCfg<T, D>;
   using Op = typename V8<T>::type;
   constexpr int BM = C::BM, BN = C::BN, KS = C::KS, DB = C::DB;
+  constexpr int sz = (int)sizeof(T);
   __shared__ __attribute__((aligned(16))) char smem[C::LDS];
-  auto kbuf = [&](int s) { return reinterpret_cast<T*>(smem + s * C::STAGE); };
-  auto vbuf = [&](int s) { return reinterpret_cast<T*>(smem + s * C::STAGE) + BN * C::KSTR; };
+  const unsigned sbase = lds_addr(smem);
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int BH = a.B * a.H;
   const int trank = blockIdx.x / BH, bh = blockIdx.x % BH, b = bh / a.H, h = bh % a.H;
   const Geo geo{a.layout, a.cp, a.rank, a.T, a.Tkv};
@@ -451,8 +356,13 @@ __global__ __launch_bounds__(256, E3_DQ_OCC) void dq_kernel(const Args a) {
   const long long rs = (long long)a.H * D;
   const T* qb = reinterpret_cast<const T*>(a.q) + (long long)b * a.T * rs + (long long)h * D;
   const T* dob = reinterpret_cast<const T*>(a.dout) + (long long)b * a.T * rs + (long long)h * D;
-  const T* k0b = reinterpret_cast<const T*>(a.k0) + (long long)b * a.k0_bs + (long long)h * D;
-  const T* v0b = reinterpret_cast<const T*>(a.v0) + (long long)b * a.k0_bs + (long long)h * D;
+  const char* const kbytes =
+      reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.k0) + (long long)b * a.k0_bs + (long long)h * D);
+  const char* const vbytes =
+      reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.v0) + (long long)b * a.k0_bs + (long long)h * D);
+  const char* const ktbytes =
+      reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.kt) + (long long)bh * D * a.kv_pitch);
+  const unsigned krow = (unsigned)(rs * sz), trow = (unsigned)((long long)a.kv_pitch * sz);
   // lse2 / delta rows in the padded layout; the tile lies inside one run.
   const float* lseb = a.lse2 + (long long)bh * a.q_pitch + (geo.prow(row0) - row0);
   const float* delb = a.delta + (long long)bh * a.q_pitch + (geo.prow(row0) - row0);
@@ -481,80 +391,72 @@ __global__ __launch_bounds__(256, E3_DQ_OCC) void dq_kernel(const Args a) {
     for (int j = 0; j < 16; ++j) acc[db][j] = 0.f;
   const float c2 = a.c2;
 
-  SegIter it;
-  it.begin(geo, lo_min, g_max + 1, BN);
-  TileLoad<T, BN, D, 256> kt, vt;
-  auto fetch = [&](int s0) {
-    const int nv = a.Tkv - s0;
-    if (nv >= BN) {
-      kt.load_full(k0b + (long long)s0 * rs, rs, tid);
-      vt.load_full(v0b + (long long)s0 * rs, rs, tid);
-    } else {
-      kt.load(k0b + (long long)s0 * rs, rs, nv, tid);
-      vt.load(v0b + (long long)s0 * rs, rs, nv, tid);
+  // Stage p: K rows at 0, V rows at KT, K^T at 2 KT (swizzled, direct copies).
+  // K / V rows past the end re-read the last row: those keys are masked.
+  auto dma_stage = [&](int p, int s0) {
+    const unsigned st = sbase + (unsigned)(p * C::STAGE);
+    const int nv = a.Tkv - s0 < BN ? a.Tkv - s0 : BN;
+    dma_tile<BN, C::KRB, C::U>(st, kbytes + (long long)s0 * krow, krow, nv, w, lane);
+    dma_tile<BN, C::KRB, C::U>(st + C::KT, vbytes + (long long)s0 * krow, krow, nv, w, lane);
+    dma_tile<D, C::TRB, C::U>(st + 2 * C::KT, ktbytes + (long long)s0 * sz, trow, D, w, lane);
+  };
+  auto interior = [&](const SegIter& t) {
+    return t.s0 >= t.a && t.s0 + BN <= t.b && t.s0 >= lo_max && t.s0 + BN - 1 <= g_min;
+  };
+  // Key s = t.s0 + 4g + o (o = 8(j/4) + j%4) is visible when lo <= o <= hi.
+  auto mask = [&](f32x16& st, const SegIter& t) {
+    const int base = t.s0 + 4 * g;
+    const int lo = (t.a > loq ? t.a : loq) - base;
+    const int hi = ((t.b - 1) < gq ? (t.b - 1) : gq) - base;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int o = 8 * (j >> 2) + (j & 3);
+      st[j] = (o >= lo && o <= hi) ? st[j] : kNegInf;
     }
   };
-  int stage = 0;
-  if (it.valid) {
-    fetch(it.s0);
-    kt.store(kbuf(0), C::KSTR, tid);
-    vt.store(vbuf(0), C::VSTR, tid);
-  }
-  SegIter nx = it;
-  if (nx.valid) nx.next(geo, BN);
-  if (nx.valid) fetch(nx.s0);
+
+  SegIter it, i1;
+  it.begin(geo, lo_min, g_max + 1, BN);
+  i1 = it;
+  if (i1.valid) i1.next(geo, BN);
+  if (it.valid) dma_stage(0, it.s0);
   wait_all();
   __syncthreads();
 
-  while (it.valid) {
-    const int s0 = it.s0, sa = it.a, sb = it.b;
-    const T* Ks = kbuf(stage);
-    const T* Vs = vbuf(stage);
-
-    // One 32-key block at a time: S^T, dP^T, then dS^T as two MFMA operands.
-    const bool interior = s0 >= sa && s0 + BN <= sb && s0 >= lo_max && s0 + BN - 1 <= g_min;
-    Op dsop[BN / 16];
+  for (int par = 0; it.valid; par ^= 1) {
+    const int cur = __builtin_amdgcn_readfirstlane(par);
+    const char* const Ks = smem + cur * C::STAGE;
+    const char* const Vs = Ks + C::KT;
+    const char* const KTs = Ks + 2 * C::KT;
+    if (i1.valid) dma_stage(cur ^ 1, i1.s0);
+    // S^T and dP^T for the 32 keys: lane = query.
+    f32x16 st, dpt;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      f32x16 st, dpt;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        st[j] = 0.f;
-        dpt[j] = 0.f;
-      }
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        mfma16(lds_row8(Ks, C::KSTR, 32 * kb + l32, 16 * ks + 8 * g), qreg[ks], st);
-        mfma16(lds_row8(Vs, C::VSTR, 32 * kb + l32, 16 * ks + 8 * g), oreg[ks], dpt);
-      }
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        float p = fast_exp2(fmaf(st[j], c2, -lq));
-        if (!interior) {
-          const int s = s0 + 32 * kb + 8 * (j >> 2) + 4 * g + (j & 3);
-          const bool vis = s >= sa && s < sb && s >= loq && s <= gq;
-          p = vis ? p : 0.f;
-        }
-        dpt[j] = p * (dpt[j] - dq_delta);
-      }
-      dsop[2 * kb] = to_op(dpt, 0, T());
-      dsop[2 * kb + 1] = to_op(dpt, 8, T());
+    for (int j = 0; j < 16; ++j) {
+      st[j] = 0.f;
+      dpt[j] = 0.f;
     }
-    // dQ^T += K^T dS^T over the 64 keys (4 k-steps of 16).
 #pragma unroll
-    for (int ks = 0; ks < BN / 16; ++ks)
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-        mfma16(lds_col8(Ks, C::KSTR, 16 * ks, 32 * db, lane), dsop[ks], acc[db]);
-
-    it = nx;
-    if (it.valid) {
-      kt.store(kbuf(stage ^ 1), C::KSTR, tid);
-      vt.store(vbuf(stage ^ 1), C::VSTR, tid);
-      nx.next(geo, BN);
-      if (nx.valid) fetch(nx.s0);
+    for (int ks = 0; ks < KS; ++ks) {
+      mfma16(lds_sw8<T, C::KRB>(Ks, l32, 16 * ks + 8 * g), qreg[ks], st);
+      mfma16(lds_sw8<T, C::KRB>(Vs, l32, 16 * ks + 8 * g), oreg[ks], dpt);
     }
-    stage ^= 1;
+    if (!interior(it)) mask(st, it);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const float p = fast_exp2(fmaf(st[j], c2, -lq));
+      dpt[j] = p * (dpt[j] - dq_delta);
+    }
+    const Op ds0 = to_op(dpt, 0, T()), ds1 = to_op(dpt, 8, T());
+    // dQ^T += K^T dS^T over the 32 keys (2 k-steps of 16).
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      mfma16(lds_sw8<T, C::TRB>(KTs, 32 * db + l32, 8 * g), ds0, acc[db]);
+      mfma16(lds_sw8<T, C::TRB>(KTs, 32 * db + l32, 16 + 8 * g), ds1, acc[db]);
+    }
+    it = i1;
+    if (i1.valid) i1.next(geo, BN);
+    wait_all();
     __syncthreads();
   }
 
@@ -573,38 +475,66 @@ __global__ __launch_bounds__(256, E3_DQ_OCC) void dq_kernel(const Args a) {
     }
   __syncthreads();
 
-  // All kd/vd loads of a group of NB blocks are issued before any is used.
+  // scale * dQ(block 0): the final dq when there are no diagonal blocks, else a
+  // float32 partial that diag_bwd_kernel completes.
   constexpr int LPR = D / 8;
   constexpr int RPP = 64 / LPR;
-  constexpr int NB = C::NB;
-  using V = typename V8<T>::type;
   const int lr = lane / LPR, cc = (lane % LPR) * 8;
-  const T* kdb = reinterpret_cast<const T*>(a.kd) + (long long)b * a.kd_bs + (long long)h * D + cc;
-  const T* vdb = reinterpret_cast<const T*>(a.vd) + (long long)b * a.kd_bs + (long long)h * D + cc;
-  T* dkdb = reinterpret_cast<T*>(a.dkd) + (long long)b * a.kd_bs + (long long)h * D + cc;
-  T* dvdb = reinterpret_cast<T*>(a.dvd) + (long long)b * a.kd_bs + (long long)h * D + cc;
   T* dqb = reinterpret_cast<T*>(a.dq) + (long long)b * a.T * rs + (long long)h * D + cc;
-  const float scale = a.scale;
+  float* dqdb = const_cast<float*>(a.dqd) + (long long)b * a.T * rs + (long long)h * D + cc;
   for (int pass = 0; pass < 32 / RPP; ++pass) {
     const int rr = pass * RPP + lr;
     const int tr = w * 32 + rr;
-    const bool ok = tr < nrows;              // whole row groups agree
-    const long long row = row0 + (ok ? tr : 0);
+    if (tr >= nrows) continue;               // whole row groups agree
+    const long long row = row0 + tr;
     f32x8 dqv = *reinterpret_cast<const f32x8*>(Qw + rr * C::OSTR + cc);
-    const V qv = load8(qb + row * rs + cc);
-    const V ov = load8(dob + row * rs + cc);
-    const float l2 = lseb[row];
-    const float dl = delb[row];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dqv[e] *= a.scale;
+    if (a.N > 0) *reinterpret_cast<f32x8*>(dqdb + row * rs) = dqv;
+    else store8f(dqb + row * rs, dqv);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Closed-form diagonal gradients (ring_attention page, `_merge_diag`: each
+// position's TTT blocks are one score each), against the merged lse:
+//   pi = exp(y - lse), dpi = <dO, vd>, ds = pi (dpi - delta),
+//   dkd = scale ds q, dvd = pi dO, dq_diag = scale sum_i ds_i kd_i (float32).
+// LPR lanes per (b, t, h) row, 8 columns each; a persistent grid strides over
+// the rows. It only reads q, dO, lse2, delta, kd, vd, so it runs on a side
+// stream next to the dK/dV kernel, whose CUs it shares (few registers, no LDS).
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(256, 4) void diag_bwd_kernel(const Args a) {
+  constexpr int LPR = D / 8;
+  constexpr int GPB = 256 / LPR;           // row groups per workgroup
+  constexpr int NB = sizeof(T) == 2 ? 4 : 2;   // blocks per load group (fits 128 VGPRs)
+  using V = typename V8<T>::type;
+  const Geo geo{a.layout, a.cp, a.rank, a.T, a.Tkv};
+  const int tid = threadIdx.x, cc = (tid % LPR) * 8;
+  const long long nrow = (long long)a.B * a.T * a.H;
+  const long long rs = (long long)a.H * D;
+  const float c2 = a.c2, scale = a.scale;
+  for (long long r = (long long)blockIdx.x * GPB + tid / LPR; r < nrow; r += (long long)gridDim.x * GPB) {
+    const int h = (int)(r % a.H);
+    const long long bt = r / a.H;
+    const int t = (int)(bt % a.T), b = (int)(bt / a.T);
+    const long long qoff = r * D + cc;                         // [B,T,H,D] row
+    const long long doff = (long long)b * a.kd_bs + ((long long)t * a.H + h) * D + cc;
+    const long long loff = ((long long)b * a.H + h) * a.q_pitch + geo.prow(t);
+    const V qv = load8(reinterpret_cast<const T*>(a.q) + qoff);
+    const V ov = load8(reinterpret_cast<const T*>(a.dout) + qoff);
+    const float l2 = a.lse2[loff], dl = a.delta[loff];
+    f32x8 dq = *reinterpret_cast<const f32x8*>(a.dqd + qoff);   // scale * dQ(block 0)
     for (int i0 = 0; i0 < a.N; i0 += NB) {
       const int n = (a.N - i0) < NB ? (a.N - i0) : NB;
-      // Unconditional loads (block index clamped): conditional ones would be
-      // waited for one at a time.
+      // Unconditional loads (block index clamped), all issued before any use.
       V kv[NB], vv[NB];
 #pragma unroll
       for (int i = 0; i < NB; ++i) {
-        const long long off = (long long)(i0 + (i < n ? i : n - 1)) * a.kd_blk + row * rs;
-        kv[i] = load8(kdb + off);
-        vv[i] = load8(vdb + off);
+        const long long off = (long long)(i0 + (i < n ? i : n - 1)) * a.kd_blk + doff;
+        kv[i] = load8_nt(reinterpret_cast<const T*>(a.kd) + off);
+        vv[i] = load8_nt(reinterpret_cast<const T*>(a.vd) + off);
       }
 #pragma unroll
       for (int i = 0; i < NB; ++i) {
@@ -616,61 +546,69 @@ __global__ __launch_bounds__(256, E3_DQ_OCC) void dq_kernel(const Args a) {
         f32x8 gk, gv;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          dqv[e] = fmaf(ds, (float)kv[i][e], dqv[e]);
+          dq[e] = fmaf(sds, (float)kv[i][e], dq[e]);
           gk[e] = sds * (float)qv[e];
           gv[e] = pi * (float)ov[e];
         }
-        if (ok && i < n) {
-          const long long off = (long long)(i0 + i) * a.kd_blk + row * rs;
-          store8f(dkdb + off, gk);
-          store8f(dvdb + off, gv);
+        if (i < n) {
+          const long long off = (long long)(i0 + i) * a.kd_blk + doff;
+          store8f_nt(reinterpret_cast<T*>(a.dkd) + off, gk);
+          store8f_nt(reinterpret_cast<T*>(a.dvd) + off, gv);
         }
       }
     }
-    if (ok) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) dqv[e] *= scale;
-      store8f(dqb + row * rs, dqv);
-    }
+    store8f(reinterpret_cast<T*>(a.dq) + qoff, dq);
   }
 }
 
+// Order (marks between the stages for the timing hook):
+//   main:  delta | K^T | dQ | (join Q^T, dO^T) dK/dV | (join diagonal)
+//   side:          Q^T, dO^T                 ... diagonal gradients (after dQ)
+// The Q^T / dO^T transposes overlap the dQ kernel and the diagonal gradients
+// (memory-bound) overlap the dK/dV kernel.
 template <typename T, int D>
 static hipError_t launch_bwd_t(const Args& a, hipStream_t st) {
   const Geo geo{a.layout, a.cp, a.rank, a.T, a.Tkv};
   const long long nrow = (long long)a.B * a.H * a.q_pitch;
   if (nrow == 0) return hipSuccess;
+  const int dt = sizeof(T) == 2 ? 0 : 1;
+  const long long qbs = (long long)a.T * a.H * D;
+  hipError_t e;
   timing_mark(st);
   {
     const long long nb = (nrow + (256 / (D / 8)) - 1) / (256 / (D / 8));
     hipLaunchKernelGGL((delta_kernel<T, D>), dim3((unsigned)nb), dim3(256), 0, st, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   timing_mark(st);
-  {
-    const long long qbs = (long long)a.T * a.H * D;
-    hipError_t e = launch_xpose(a.q, qbs, const_cast<void*>(a.qt), geo.qruns(), a.B, a.H,
-                                sizeof(T) == 2 ? 0 : 1, D, st);
-    if (e == hipSuccess)
-      e = launch_xpose(a.dout, qbs, const_cast<void*>(a.dot), geo.qruns(), a.B, a.H,
-                       sizeof(T) == 2 ? 0 : 1, D, st);
-    if (e != hipSuccess) return e;
-  }
-  timing_mark(st);
-  const long long nk = (long long)((a.Tkv + DkdvCfg<T, D>::BNK - 1) / DkdvCfg<T, D>::BNK) * a.B * a.H;
-  if (nk > 0) {
-    hipLaunchKernelGGL((dkdv_kernel<T, D>), dim3((unsigned)nk), dim3(256), 0, st, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
+  hipStream_t side = nullptr;
+  if ((e = side_begin(st, 0, side)) != hipSuccess) return e;
+  if ((e = launch_xpose(a.q, qbs, const_cast<void*>(a.qt), geo.qruns(), a.B, a.H, dt, D, side)) != hipSuccess)
+    return e;
+  if ((e = launch_xpose(a.dout, qbs, const_cast<void*>(a.dot), geo.qruns(), a.B, a.H, dt, D, side)) != hipSuccess)
+    return e;
+  if ((e = launch_xpose(a.k0, a.k0_bs, const_cast<void*>(a.kt), geo.kvruns(), a.B, a.H, dt, D, st)) != hipSuccess)
+    return e;
   timing_mark(st);
   const long long nq = (long long)geo.ntiles(DqCfg<T, D>::BM) * a.B * a.H;
   if (nq > 0) {
     hipLaunchKernelGGL((dq_kernel<T, D>), dim3((unsigned)nq), dim3(256), 0, st, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
+  timing_mark(st);
+  if ((e = side_end(st, 0)) != hipSuccess) return e;
+  if (a.N > 0) {
+    if ((e = side_begin(st, 1, side)) != hipSuccess) return e;
+    hipLaunchKernelGGL((diag_bwd_kernel<T, D>), dim3(kDiagGrid), dim3(256), 0, side, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  const long long nk = (long long)((a.Tkv + DkdvCfg<T, D>::BNK - 1) / DkdvCfg<T, D>::BNK) * a.B * a.H;
+  if (nk > 0) {
+    hipLaunchKernelGGL((dkdv_kernel<T, D>), dim3((unsigned)nk), dim3(DkdvCfg<T, D>::NT), 0, st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  timing_mark(st);
+  if (a.N > 0 && (e = side_end(st, 1)) != hipSuccess) return e;
   timing_mark(st);
   return hipSuccess;
 }

@@ -36,6 +36,7 @@ struct Args {
   float* lse;
   float* delta;         // rowsum(dO * O), [B, H, q_pitch] (rows at Geo::prow)
   float* lse2;          // lse * log2(e), same layout as delta (delta = lse2 + B*H*q_pitch)
+  const float* dqd;     // diagonal part of dq, float32 [B, T, H, D] (backward workspace)
   void* dq;
   void* dk0;
   void* dv0;
@@ -82,6 +83,16 @@ __host__ __device__ inline int tile_order(int o, int n) {
 // Measurement hook (host): records the next caller-provided timing event, if any,
 // on the stream. Called before the first kernel of an entry point and after each.
 void timing_mark(hipStream_t st);
+
+// A side stream (per host thread and device, created on first use and kept,
+// default priority) for work that overlaps the caller's stream.
+// side_begin(main, k, side): the side stream waits for all work queued on
+// `main` so far; side_end(main, k): `main` waits for all work queued on the side
+// stream so far. k (0 or 1) selects the event pair, so two fork/join pairs can
+// be in flight in one call.
+hipError_t side_begin(hipStream_t main, int k, hipStream_t& side);
+hipError_t side_end(hipStream_t main, int k);
+constexpr int kDiagGrid = 256;   // persistent grid of the diagonal-gradient kernel
 
 // Writes the transposed copy of x [B, rows, H, D] (batch stride x_bs) laid out by runs.
 hipError_t launch_xpose(const void* x, long long x_bs, void* xt, const XRuns& runs, int B, int H,
@@ -423,6 +434,19 @@ __device__ __forceinline__ void store8f(T* p, const f32x8& v) {
   for (int i = 0; i < 8; ++i) r[i] = (T)v[i];
   *reinterpret_cast<typename V8<T>::type*>(p) = r;
 }
+// Streaming (non-temporal) variants, for data touched once, so that it does
+// not evict the working set of kernels running alongside.
+template <typename T>
+__device__ __forceinline__ typename V8<T>::type load8_nt(const T* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const typename V8<T>::type*>(p));
+}
+template <typename T>
+__device__ __forceinline__ void store8f_nt(T* p, const f32x8& v) {
+  typename V8<T>::type r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (T)v[i];
+  __builtin_nontemporal_store(r, reinterpret_cast<typename V8<T>::type*>(p));
+}
 
 // ---------------------------------------------------------------------------
 // Global -> LDS tile staging. A tile is R rows x D columns of T kept in LDS in
@@ -564,21 +588,21 @@ __device__ __forceinline__ void lds_dma16(const char* base, unsigned voff, unsig
 // lane i fetches the chunk that belongs in that slot. Row r of the tile is read
 // at `base` + r * `stride` bytes (base uniform, the per-lane part 32-bit); rows
 // at or past `nvalid` re-read row nvalid - 1. The copies complete
-// asynchronously (vmcnt). 4 waves per workgroup split the instructions; `w`
-// (the wave index) should be wave-uniform in a scalar register.
-template <int R, int RB>
+// asynchronously (vmcnt). The NW waves of the workgroup split the
+// instructions; `w` (the wave index) should be wave-uniform in a scalar register.
+template <int R, int RB, int NW = 4>
 struct DmaShape {
   static constexpr int CPR = RB / 16;     // chunks per row
   static constexpr int RPI = 64 / CPR;    // rows per wave instruction
-  static constexpr int NI = R / RPI / 4;  // instructions per wave
-  static_assert(NI >= 1 && NI * RPI * 4 == R, "tile does not split over 4 waves");
+  static constexpr int NI = R / RPI / NW; // instructions per wave
+  static_assert(NI >= 1 && NI * RPI * NW == R, "tile does not split over the waves");
 };
 
-// Instruction i (0 <= i < NI) of this wave's share of the copy.
-template <int R, int RB, int U>
+// Instruction i (0 <= i < NI) of this wave's share of the copy (NW waves).
+template <int R, int RB, int U, int NW = 4>
 __device__ __forceinline__ void dma_tile_part(unsigned lds, const char* base, unsigned stride,
                                               int nvalid, int w, int lane, int i) {
-  using S = DmaShape<R, RB>;
+  using S = DmaShape<R, RB, NW>;
   const int r0 = (w * S::NI + i) * S::RPI;
   const int rl = lane / S::CPR;
   if (nvalid >= R) {
@@ -594,11 +618,12 @@ __device__ __forceinline__ void dma_tile_part(unsigned lds, const char* base, un
   }
 }
 
-template <int R, int RB, int U>
+template <int R, int RB, int U, int NW = 4>
 __device__ __forceinline__ void dma_tile(unsigned lds, const char* base, unsigned stride, int nvalid,
                                          int w, int lane) {
 #pragma unroll
-  for (int i = 0; i < DmaShape<R, RB>::NI; ++i) dma_tile_part<R, RB, U>(lds, base, stride, nvalid, w, lane, i);
+  for (int i = 0; i < DmaShape<R, RB, NW>::NI; ++i)
+    dma_tile_part<R, RB, U, NW>(lds, base, stride, nvalid, w, lane, i);
 }
 
 // MFMA operand of 8 consecutive elements (columns col..col+7) of row `row` of a

@@ -30,9 +30,14 @@
  *     gradients. out is returned in q's dtype (ulysses_attention page,
  *     `cached_ulysses_attention`); all merging is done in float32.
  *   - Every pointer passed to a compute entry point is a DEVICE pointer unless named
- *     *_host. The caller owns (allocates and frees) every buffer, including the backward
- *     workspace. The library allocates nothing and keeps no per-call state.
- *   - Calls are asynchronous on the given HIP stream and never synchronise.
+ *     *_host. The caller owns (allocates and frees) every buffer, including the
+ *     workspaces. The library allocates no device memory and keeps no per-call state.
+ *   - Calls are asynchronous on the given HIP stream and never synchronise. The backward
+ *     forks part of its work (the diagonal-block gradients) onto a side stream that
+ *     waits for the given stream and is joined back into it before the call's last
+ *     kernel, so the result is ordered on the given stream as if all ran there. The side
+ *     stream and its two events are created on first use, one set per host thread and
+ *     device, and kept until the process ends.
  *   - Every output is overwritten; rows of dk0/dv0 that no local query sees are written
  *     as zeros.
  *   - Errors: arguments are validated before anything is launched. On failure a negative
@@ -111,9 +116,10 @@ int eagle3_abi_version(void);
 const char* eagle3_last_error(void);
 
 /* Bytes of device workspace eagle3_attn_bwd / eagle3_shard_bwd need: delta = rowsum(dO*O)
- * and lse*log2(e) (float32 [B, H, P]) and transposed copies of q and dout (dtype
+ * and lse*log2(e) (float32 [B, H, P]), transposed copies of q and dout (dtype
  * [B, H, D, P]), P = T with each local run (the two zig-zag chunks) padded to a multiple
- * of 64 positions. 0 when T == 0. Returns 0 and sets the last error for an invalid
+ * of 64 positions, and a transposed copy of k0 (dtype [B, H, D, P_kv], P_kv = T_kv
+ * rounded up to 64). 0 when T == 0. Returns 0 and sets the last error for an invalid
  * problem. */
 size_t eagle3_bwd_workspace_bytes(const e3_problem* p);
 
@@ -171,8 +177,8 @@ int lse_merge(float* out, float* lse, const float* block_out, const float* block
 /* While `events` is non-NULL, every compute entry point called on this thread records
  * events[0] on its stream before its first kernel and events[k+1] after its k-th stage
  * (at most `capacity` events; the forward has 2 stages: the V transpose and the
- * attention kernel; the backward 4: delta and lse*log2(e), the Q and dO transposes,
- * dK/dV, dQ). The caller creates and owns the events; NULL stops recording. Returns
+ * attention kernel; the backward 5: delta and lse*log2(e), the K transpose, dQ,
+ * dK/dV, and the wait for the side stream's diagonal-block gradients). The caller creates and owns the events; NULL stops recording. Returns
  * E3_OK. */
 int eagle3_set_timing_events(hipEvent_t* events, int capacity);
 

@@ -102,14 +102,18 @@ def test_null_and_misaligned_pointers_are_rejected():
 
 def test_workspace_bytes():
     p = prob(B=1, T=1000, T_kv=1000, H=3)
-    # backward: lse2 and delta (float32 [B, H, P]) and transposed q and dout (bf16
-    # [B, H, D, P]), P = T rounded up to 64 (one run)
+    # backward: lse2 and delta (float32 [B, H, P]), transposed q and dout (bf16
+    # [B, H, D, P]), P = T rounded up to 64 (one run), and transposed k0 (bf16
+    # [B, H, D, P_kv], P_kv = T_kv rounded up to 64)
     P = 1024
-    assert p.workspace_bytes() == 2 * 1 * 3 * P * 4 + 2 * 1 * 3 * 128 * P * 2
+    # and, with diagonal blocks, the diagonal part of dq (float32 [B, T, H, D])
+    assert p.workspace_bytes() == (2 * 1 * 3 * P * 4 + 2 * 1 * 3 * 128 * P * 2 + 1 * 3 * 128 * P * 2
+                                   + 1 * 1000 * 3 * 128 * 4)
     # zig-zag: each of the two local chunks is padded to 64 rows on its own
     zz = e3.Problem(1, 300, 3 * 300, 3, 128, 3, 0.1, layout="zigzag", cp=3, rank=2)
-    Pz = 2 * 192
-    assert zz.workspace_bytes() == 2 * 3 * Pz * 4 + 2 * 3 * 128 * Pz * 2
+    Pz, Pkv = 2 * 192, 960
+    assert zz.workspace_bytes() == (2 * 3 * Pz * 4 + 2 * 3 * 128 * Pz * 2 + 3 * 128 * Pkv * 2
+                                    + 300 * 3 * 128 * 4)
     # transposed v0: [B, H, D, T_kv rounded up to 64], bf16
     assert p.fwd_workspace_bytes() == ((1 * 3 * 128 * 1024 * 2 + 255) // 256) * 256
 

@@ -436,11 +436,13 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const Args a) {
       st[j] = 0.f;
       dpt[j] = 0.f;
     }
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      mfma16(lds_sw8<T, C::KRB>(Ks, l32, 16 * ks + 8 * g), qreg[ks], st);
-      mfma16(lds_sw8<T, C::KRB>(Vs, l32, 16 * ks + 8 * g), oreg[ks], dpt);
-    }
+    // MFMA i: k-step i / 2, S (even, rows of K) or dP (odd, rows of V).
+    mfma_ring<2 * KS, 3>(
+        [&](int i) { return lds_sw8<T, C::KRB>((i & 1) ? Vs : Ks, l32, 16 * (i >> 1) + 8 * g); },
+        [&](int i, const Op& op) {
+          if (i & 1) mfma16(op, oreg[i >> 1], dpt);
+          else mfma16(op, qreg[i >> 1], st);
+        });
     if (!interior(it)) mask(st, it);
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
@@ -449,11 +451,10 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const Args a) {
     }
     const Op ds0 = to_op(dpt, 0, T()), ds1 = to_op(dpt, 8, T());
     // dQ^T += K^T dS^T over the 32 keys (2 k-steps of 16).
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      mfma16(lds_sw8<T, C::TRB>(KTs, 32 * db + l32, 8 * g), ds0, acc[db]);
-      mfma16(lds_sw8<T, C::TRB>(KTs, 32 * db + l32, 16 + 8 * g), ds1, acc[db]);
-    }
+    // MFMA i: 32-row block i / 2 of D, k-step i % 2 over the 32 keys.
+    mfma_ring<2 * DB, 3>(
+        [&](int i) { return lds_sw8<T, C::TRB>(KTs, 32 * (i >> 1) + l32, 16 * (i & 1) + 8 * g); },
+        [&](int i, const Op& op) { mfma16(op, (i & 1) ? ds1 : ds0, acc[i >> 1]); });
     it = i1;
     if (i1.valid) i1.next(geo, BN);
     wait_all();

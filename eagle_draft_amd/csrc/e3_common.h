@@ -36,7 +36,8 @@ struct Args {
   float* lse;
   float* delta;         // rowsum(dO * O), [B, H, q_pitch] (rows at Geo::prow)
   float* lse2;          // lse * log2(e), same layout as delta (delta = lse2 + B*H*q_pitch)
-  const float* dqd;     // diagonal part of dq, float32 [B, T, H, D] (backward workspace)
+  const float* dqd;     // float32 partial of dq from the dQ kernel, [B, T, H, D] (workspace)
+  const float* dqg;     // float32 diagonal part of dq, [B, T, H, D] (workspace)
   void* dq;
   void* dk0;
   void* dv0;
@@ -624,6 +625,23 @@ __device__ __forceinline__ void dma_tile(unsigned lds, const char* base, unsigne
 #pragma unroll
   for (int i = 0; i < DmaShape<R, RB, NW>::NI; ++i)
     dma_tile_part<R, RB, U, NW>(lds, base, stride, nvalid, w, lane, i);
+}
+
+// Runs the n MFMAs of a phase with their LDS operands read A steps ahead into a
+// ring, one fence per step so the compiler keeps the reads ahead:
+// `read(i)` returns operand i, `mma(i, op)` issues MFMA i.
+template <int N, int A, typename Read, typename Mma>
+__device__ __forceinline__ void mfma_ring(Read read, Mma mma) {
+  using Op = decltype(read(0));
+  Op ring[A + 1];
+#pragma unroll
+  for (int i = 0; i < A && i < N; ++i) ring[i] = read(i);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    if (i + A < N) ring[(i + A) % (A + 1)] = read(i + A);
+    mma(i, ring[i % (A + 1)]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
 }
 
 // MFMA operand of 8 consecutive elements (columns col..col+7) of row `row` of a

@@ -15,8 +15,11 @@ from __future__ import annotations
 
 import argparse
 import ctypes
+import glob
+import hashlib
 import json
 import os
+import re
 import statistics
 import sys
 import time
@@ -33,6 +36,42 @@ KERNELS = ["xpose_v", "fwd", "delta", "xpose_k", "dq", "dkdv", "diag_tail"]
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
+
+
+def sources_sha256():
+    """Hash of the kernel sources (the HIP files, the C ABI and its header)."""
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(ROOT, "eagle_draft_amd", "csrc", "*")) +
+                   glob.glob(os.path.join(ROOT, "include", "*.h")))
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(stage):
+    """HBM bytes per launch of the stage's kernel from the counter summary in
+    profiles/ (FETCH_SIZE and WRITE_SIZE, each divided by the factor the same
+    counter reads on a plain copy of known size), or None when there is none for
+    this stage or the kernel sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "dense_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as fh:
+        for line in fh:
+            m = re.match(r"^- (\w+): (\S+)", line.strip())
+            if m:
+                kv[m.group(1)] = m.group(2)
+    try:
+        if kv.get("stage") != stage or kv.get("sources_sha256") != sources_sha256():
+            return None
+        fetch = float(kv["fetch_bytes_per_launch"]) / float(kv["copy_fetch_factor"])
+        write = float(kv["write_bytes_per_launch"]) / float(kv["copy_write_factor"])
+    except (KeyError, ValueError):
+        return None
+    return round(fetch + write)
 
 
 def kernel_work(w, P0):
@@ -145,6 +184,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of CPU oracle work for the baseline (0 = skip)")
     ap.add_argument("--no-flush", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="run one plain device copy of this many MiB before timing (a known-size "
+                         "kernel for calibrating the HBM byte counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -187,6 +229,15 @@ def main():
         step()
     torch.cuda.synchronize()
     log(f"[bench] warmup {args.warmup} done")
+    if args.calib_copy_mib > 0:
+        n = args.calib_copy_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log(f"[bench] calibration copy of {args.calib_copy_mib} MiB done")
 
     # (1) the timed region: exactly K back-to-back steps, synchronized on both sides
     ev = HipEvents()
@@ -264,7 +315,7 @@ def main():
         roof = {"bound": "hbm", "achieved": round(dk["bytes"] / t_dom / 1e9, 1), "peak": PEAK_GBS,
                 "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(dom)
     roof["kernel"] = dom
     roof["algorithmic"] = {"flop": dk["flop"], "bytes": dk["bytes"]}
 
@@ -297,6 +348,7 @@ def main():
         "roofline": roof,
         "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
                    "compute_units": props.multi_processor_count},
+        "sources_sha256": sources_sha256(),
     }
     if args.cpu_budget > 0:
         log("[bench] timing the CPU oracle ...")

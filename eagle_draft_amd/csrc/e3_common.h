@@ -545,15 +545,16 @@ __device__ __forceinline__ f32x8 lds_col8(const float* tile, int stride, int k0,
 // sits in chunk slot c ^ sw(r). sw is a multiple of U (16-byte chunks per MFMA
 // operand: 1 for bf16, 2 for fp32), so an operand's chunks stay adjacent. The
 // masks are the ones measured fastest on gfx950 for 16-byte reads of one
-// operand column by 32 consecutive rows (per wave, 4 waves per CU: 21.7 cycles
-// per read for 256-byte rows with r mod 16, against 32 with r mod 8; 17.3 for
-// 128-byte rows with r mod 8; 12.8 for 64-byte rows with (r / 2) mod 4).
+// operand column by 32 consecutive rows (4 waves per CU: 21.7 cycles per read
+// per wave for 256-byte rows with r mod 16, against 32 with r mod 8; 17.3 for
+// 128-byte rows with r mod 8; with 8 waves per CU all three reach the LDS peak of
+// ~256 B/clk, 64-byte rows only with (r / 4) mod 4).
 template <int RB, int U>
 __device__ __forceinline__ int sw_mask(int r) {
   constexpr int CPR = RB / 16;
   if constexpr (CPR >= 16) return ((r & 15) * U) & (CPR - 1);
   else if constexpr (CPR == 8) return ((r & 7) * U) & 7;
-  else return (((r >> 1) & 3) * U) & (CPR - 1);
+  else return (((r >> 2) & 3) * U) & (CPR - 1);
 }
 
 // LDS byte address of a pointer into __shared__ memory.

@@ -31,7 +31,9 @@ if ROOT not in sys.path:
 METRIC = "EAGLE-3 mixed attn fwd+bwd TFLOP/s (causal) + % bf16 MFMA peak, T=4096 H=32 D=128"
 PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}   # MI355X dense MFMA (bf16) / fp32 vector
 PEAK_GBS = 8000.0                               # MI355X HBM3E
-KERNELS = ["xpose_v", "fwd", "delta", "xpose_k", "dq", "dkdv", "diag_tail"]
+KERNELS = ["fwd", "delta", "dq", "dkdv", "diag_tail"]
+FWD_STAGES = ["fwd"]
+BWD_STAGES = ["delta", "dq", "dkdv", "diag_tail"]
 
 
 def log(msg):
@@ -85,15 +87,10 @@ def kernel_work(w, P0):
     pf = B * H * D * P0                       # one D-long dot per attended pair
     diagf = B * H * D * T * N
     return {
-        # v0 read, its transposed copy written
-        "xpose_v": dict(flop=0, diag_flop=0, bytes=2 * ukv),
         # q, k0, v0, kd, vd read; out, lse written
         "fwd": dict(flop=4 * pf, diag_flop=4 * diagf, bytes=u + 2 * ukv + 2 * N * u + u + rowf),
         # dO, O, lse read; delta and lse*log2(e) written
         "delta": dict(flop=0, diag_flop=0, bytes=2 * u + 3 * rowf),
-        # k0 read, its transposed copy written (the q and dO transposes run on the
-        # side stream during dq and are not in any stage)
-        "xpose_k": dict(flop=0, diag_flop=0, bytes=2 * ukv),
         # q, dO, k0, v0, lse, delta read; dk0, dv0 written; S, dP, dV, dK = 4 GEMMs
         # (the diagonal-gradient kernel runs alongside on the side stream)
         "dkdv": dict(flop=8 * pf, diag_flop=0, bytes=2 * u + 4 * ukv + 2 * rowf),
@@ -217,11 +214,10 @@ def main():
     grads = (torch.empty_like(d["q"]), torch.empty_like(d["k0"]), torch.empty_like(d["v0"]),
              torch.empty_like(d["kd"]), torch.empty_like(d["vd"]))
     ws = torch.empty(max(prob.workspace_bytes(), 256), dtype=torch.uint8, device=dev)
-    fws = torch.empty(max(prob.fwd_workspace_bytes(), 256), dtype=torch.uint8, device=dev)
     lib = e3.lib()
 
     def step():
-        e3.fwd(prob, d["q"], d["k0"], d["v0"], d["kd"], d["vd"], out=out, lse=lse, workspace=fws)
+        e3.fwd(prob, d["q"], d["k0"], d["v0"], d["kd"], d["vd"], out=out, lse=lse)
         e3.bwd(prob, d["dout"], d["q"], d["k0"], d["v0"], d["kd"], d["vd"], out, lse,
                grads=grads, workspace=ws)
 
@@ -256,7 +252,7 @@ def main():
     log(f"[bench] {args.steps} steps: {total_ms:.3f} ms ({ms_per_step:.4f} ms/step, wall {wall_ms:.1f} ms)")
 
     # (2) per-kernel times: events recorded by the library around each kernel
-    nfwd, nbwd = 3, 6
+    nfwd, nbwd = len(FWD_STAGES) + 1, len(BWD_STAGES) + 1
     per = {k: [] for k in KERNELS}
     fwd_ms, bwd_ms, flushed = [], [], []
     flush_buf = None if args.no_flush else torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -268,7 +264,7 @@ def main():
             flush_buf.zero_()     # evict L2 and MALL between steps (outside the events)
         psz = ctypes.sizeof(ctypes.c_void_p)
         lib.eagle3_set_timing_events(ctypes.c_void_p(ctypes.addressof(evf) + r * nfwd * psz), nfwd)
-        e3.fwd(prob, d["q"], d["k0"], d["v0"], d["kd"], d["vd"], out=out, lse=lse, workspace=fws)
+        e3.fwd(prob, d["q"], d["k0"], d["v0"], d["kd"], d["vd"], out=out, lse=lse)
         assert lib.eagle3_timing_events_recorded() == nfwd
         lib.eagle3_set_timing_events(ctypes.c_void_p(ctypes.addressof(evb) + r * nbwd * psz), nbwd)
         e3.bwd(prob, d["dout"], d["q"], d["k0"], d["v0"], d["kd"], d["vd"], out, lse,
@@ -279,12 +275,12 @@ def main():
     for r in range(reps):
         f0 = r * nfwd
         b0 = r * nbwd
-        per["xpose_v"].append(ev.elapsed_ms(evf[f0], evf[f0 + 1]))
-        per["fwd"].append(ev.elapsed_ms(evf[f0 + 1], evf[f0 + 2]))
-        for i, k in enumerate(["delta", "xpose_k", "dq", "dkdv", "diag_tail"]):
+        for i, k in enumerate(FWD_STAGES):
+            per[k].append(ev.elapsed_ms(evf[f0 + i], evf[f0 + i + 1]))
+        for i, k in enumerate(BWD_STAGES):
             per[k].append(ev.elapsed_ms(evb[b0 + i], evb[b0 + i + 1]))
-        fwd_ms.append(ev.elapsed_ms(evf[f0], evf[f0 + 2]))
-        bwd_ms.append(ev.elapsed_ms(evb[b0], evb[b0 + 5]))
+        fwd_ms.append(ev.elapsed_ms(evf[f0], evf[f0 + nfwd - 1]))
+        bwd_ms.append(ev.elapsed_ms(evb[b0], evb[b0 + nbwd - 1]))
         flushed.append(fwd_ms[-1] + bwd_ms[-1])
     ev.destroy(se)
     ev.destroy(evf)

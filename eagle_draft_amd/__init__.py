@@ -27,7 +27,7 @@ import torch  # loaded first: the library then shares torch's HIP runtime
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libeagle3_attn.so")
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 E3_OK, E3_EINVAL, E3_EUNSUPPORTED, E3_EHIP = 0, -1, -2, -3
 LAYOUTS = {"full": 0, "contiguous": 1, "zigzag": 2, "headshard": 3}
@@ -73,10 +73,8 @@ def _load():
     lib.eagle3_bwd_workspace_bytes.restype = ctypes.c_size_t
     for name in ("eagle3_attn_fwd", "eagle3_shard_fwd"):
         f = getattr(lib, name)
-        f.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        f.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
         f.restype = ctypes.c_int
-    lib.eagle3_fwd_workspace_bytes.argtypes = [P]
-    lib.eagle3_fwd_workspace_bytes.restype = ctypes.c_size_t
     for name in ("eagle3_attn_bwd", "eagle3_shard_bwd"):
         f = getattr(lib, name)
         f.argtypes = [P] + [vp] * 14 + [vp]
@@ -207,12 +205,6 @@ class Problem:
             _check(E3_EINVAL)
         return int(n)
 
-    def fwd_workspace_bytes(self) -> int:
-        n = _load().eagle3_fwd_workspace_bytes(self.ref())
-        if n == 0 and self.T > 0:
-            _check(E3_EINVAL)
-        return int(n)
-
 
 def _check_tensor(name, t, shape, dtype, device):
     if t is None:
@@ -232,7 +224,7 @@ def _entry(prob: Problem, kind: str):
     return getattr(_load(), f"eagle3_{'attn' if whole else 'shard'}_{kind}")
 
 
-def fwd(prob: Problem, q, k0, v0, kd=None, vd=None, out=None, lse=None, workspace=None):
+def fwd(prob: Problem, q, k0, v0, kd=None, vd=None, out=None, lse=None):
     """Forward: returns (out [B,T,H,D] in q's dtype, lse [B,H,T] float32)."""
     dev = q.device
     B, T, Tkv, H, D, N = prob.B, prob.T, prob.T_kv, prob.H, prob.D, prob.N
@@ -248,11 +240,9 @@ def fwd(prob: Problem, q, k0, v0, kd=None, vd=None, out=None, lse=None, workspac
         lse = torch.empty(B, H, T, dtype=torch.float32, device=dev)
     _check_tensor("out", out, (B, T, H, D), prob.dtype, dev)
     _check_tensor("lse", lse, (B, H, T), torch.float32, dev)
-    if workspace is None:
-        workspace = torch.empty(max(prob.fwd_workspace_bytes(), 256), dtype=torch.uint8, device=dev)
     _check(_entry(prob, "fwd")(prob.ref(), _ptr(q), _ptr(k0), _ptr(v0),
                                _ptr(kd if N > 0 else None), _ptr(vd if N > 0 else None),
-                               _ptr(out), _ptr(lse), _ptr(workspace), _stream()))
+                               _ptr(out), _ptr(lse), _stream()))
     return out, lse
 
 

@@ -154,15 +154,15 @@ int check_ptrs(const char* const* names, const void* const* ptrs, int n) {
 }
 
 int fwd_impl(const e3_problem* p, const void* q, const void* k0, const void* v0, const void* kd,
-             const void* vd, void* out, float* lse, void* ws, hipStream_t st, bool whole) {
+             const void* vd, void* out, float* lse, hipStream_t st, bool whole) {
   Resolved r;
   int rc = validate(p, r, whole);
   if (rc) return rc;
   if (p->T == 0) return ok();
   {
-    const char* names[] = {"q", "k0", "v0", "out", "lse", "workspace"};
-    const void* ptrs[] = {q, k0, v0, out, lse, ws};
-    if ((rc = check_ptrs(names, ptrs, 6))) return rc;
+    const char* names[] = {"q", "k0", "v0", "out", "lse"};
+    const void* ptrs[] = {q, k0, v0, out, lse};
+    if ((rc = check_ptrs(names, ptrs, 5))) return rc;
   }
   if (r.N > 0) {
     const char* names[] = {"kd", "vd"};
@@ -178,29 +178,25 @@ int fwd_impl(const e3_problem* p, const void* q, const void* k0, const void* v0,
   a.vd = vd;
   a.out = out;
   a.lse = lse;
-  a.vt = ws;
-  a.kv_pitch = geo_of(p).kvruns().pitch;
   hipError_t e = e3::launch_fwd(a, p->dtype, p->D, st);
   if (e != hipSuccess) return fail(E3_EHIP, "forward launch failed: %s", hipGetErrorString(e));
   return ok();
 }
 
+// Backward workspace: lse2 and delta (float [B,H,P], P = the 64-aligned per-run
+// row layout of the local queries), then the block-0 part of dq (float
+// [B,T,H,D], when there are diagonal blocks).
 struct BwdWs {
-  int pitch, kv_pitch;
-  size_t delta, qt, dot, kt, dqd, total;
+  int pitch;
+  size_t delta, dqd, total;
 };
 
 BwdWs bwd_ws_layout(const e3_problem* p) {
   BwdWs l;
   l.pitch = geo_of(p).qruns().pitch;
-  const size_t esz = p->dtype == E3_BF16 ? 2 : 4;
   const size_t rows = (size_t)p->B * p->H * l.pitch;       // multiple of 64
   l.delta = rows * sizeof(float);
-  l.qt = 2 * rows * sizeof(float);
-  l.dot = l.qt + rows * p->D * esz;
-  l.kt = l.dot + rows * p->D * esz;
-  l.kv_pitch = geo_of(p).kvruns().pitch;
-  l.dqd = l.kt + (((size_t)p->B * p->H * p->D * l.kv_pitch * esz + 255) & ~(size_t)255);
+  l.dqd = 2 * rows * sizeof(float);
   const int N = p->num_blocks - 1;
   l.total = l.dqd + (N > 0 ? (size_t)p->B * p->T * p->H * p->D * sizeof(float) : 0);
   return l;
@@ -234,19 +230,11 @@ int bwd_impl(const e3_problem* p, const void* dout, const void* q, const void* k
   a.o_in = out;
   a.lse_in = lse;
   {
-    // workspace: lse2, delta (float [B,H,P]), then Q^T and dO^T (dtype [B,H,D,P]),
-    // P = the 64-aligned per-run row layout of the local queries; then K^T (dtype
-    // [B,H,D,P_kv], P_kv = T_kv rounded up to 64) and the diagonal part of dq
-    // (float [B,T,H,D], when there are diagonal blocks).
     const BwdWs l = bwd_ws_layout(p);
     char* w = static_cast<char*>(ws);
     a.q_pitch = l.pitch;
     a.lse2 = reinterpret_cast<float*>(w);
     a.delta = reinterpret_cast<float*>(w + l.delta);
-    a.qt = w + l.qt;
-    a.dot = w + l.dot;
-    a.kt = w + l.kt;
-    a.kv_pitch = l.kv_pitch;
     a.dqd = reinterpret_cast<float*>(w + l.dqd);
   }
   a.dq = dq;
@@ -334,25 +322,16 @@ size_t eagle3_bwd_workspace_bytes(const e3_problem* p) {
   return bwd_ws_layout(p).total;
 }
 
-size_t eagle3_fwd_workspace_bytes(const e3_problem* p) {
-  Resolved r;
-  if (validate(p, r, false, false)) return 0;
-  g_err.clear();
-  if (p->T == 0) return 0;
-  const size_t esz = p->dtype == E3_BF16 ? 2 : 4;
-  const size_t n = (size_t)p->B * p->H * p->D * geo_of(p).kvruns().pitch * esz;
-  return (n + 255) & ~(size_t)255;
-}
+
 
 int eagle3_attn_fwd(const e3_problem* p, const void* q, const void* k0, const void* v0, const void* kd,
-                    const void* vd, void* out, float* lse, void* workspace, hipStream_t stream) {
-  return fwd_impl(p, q, k0, v0, kd, vd, out, lse, workspace, stream, true);
+                    const void* vd, void* out, float* lse, hipStream_t stream) {
+  return fwd_impl(p, q, k0, v0, kd, vd, out, lse, stream, true);
 }
 
 int eagle3_shard_fwd(const e3_problem* p, const void* q, const void* k0, const void* v0,
-                     const void* kd, const void* vd, void* out, float* lse, void* workspace,
-                     hipStream_t stream) {
-  return fwd_impl(p, q, k0, v0, kd, vd, out, lse, workspace, stream, false);
+                     const void* kd, const void* vd, void* out, float* lse, hipStream_t stream) {
+  return fwd_impl(p, q, k0, v0, kd, vd, out, lse, stream, false);
 }
 
 int eagle3_attn_bwd(const e3_problem* p, const void* dout, const void* q, const void* k0,

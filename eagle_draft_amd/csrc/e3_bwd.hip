@@ -9,24 +9,24 @@
 // Kernels, no atomics (every output element has one writer):
 //   delta_kernel  delta[b,h,t] = <dO_t, O_t> (O = the stored merged out) and
 //                 lse2 = lse * log2(e), in the 64-aligned per-run row layout
-//   xpose (x3)    Q^T and dO^T copies (e3_xpose.hip) for the dK/dV operands
-//                 (side stream, overlapping dQ) and the K^T copy for dQ
 //   dkdv_kernel   one workgroup per 128 block-0 keys (lane = key); loops over
 //                 the query tiles that see them:
 //                   S = Q K^T, P, dP = dO V^T, dS = P (dP - delta),
 //                   dV += P^T dO, dK += scale dS^T Q
-//                 Q / dO tiles and their transposes stream through swizzled
-//                 LDS stages filled by direct global->LDS copies; one wave of
-//                 each pair forms P and dV, the other dP, dS and dK, so the two
-//                 waves sharing a SIMD overlap their MFMA and VALU phases.
+//                 Q / dO tiles stream through swizzled LDS stages filled by
+//                 direct global->LDS copies and are read both along their rows
+//                 and, with transposing reads, down them; one wave of each pair
+//                 forms P and dV, the other dP, dS and dK, so the two waves
+//                 sharing a SIMD overlap their MFMA and VALU phases.
 //   diag_bwd_kernel  (side stream, after dQ, overlapping dK/dV) the closed-form
 //                 diagonal terms pi = exp(y - lse), dpi = <dO, vd>,
 //                 ds = pi (dpi - delta): dkd = scale ds q, dvd = pi dO, and
 //                 dq = (float32 partial from dQ) + scale sum_i ds_i kd_i
 //   dq_kernel     one workgroup per 128 query rows (lane = query, as in the
 //                 forward); loops over the visible 32-key tiles in ring order
-//                 (K, V and K^T staged in swizzled LDS by direct copies):
-//                   dQ += dS K (float32 partial when there are diagonals).
+//                 (K and V staged in swizzled LDS by direct copies; K^T read
+//                 down the K tile): dQ += dS K (float32 partial when there are
+//                 diagonals).
 #include "e3_common.h"
 
 namespace e3 {
@@ -77,10 +77,9 @@ struct DkdvCfg {
   static constexpr int KS = D / 16;
   static constexpr int DB = D / 32;
   static constexpr int U = 8 * (int)sizeof(T) / 16;     // 16-byte chunks per operand
-  static constexpr int RRB = D * (int)sizeof(T);        // row tiles Q, dO [BMQ][D]: row bytes
-  static constexpr int CRB = BMQ * (int)sizeof(T);      // column tiles Q^T, dO^T [D][BMQ]
-  static constexpr int RT = BMQ * RRB, CT = D * CRB;     // bytes per tile
-  static constexpr int STAGE = 2 * RT + 2 * CT;         // Q, dO, Q^T, dO^T
+  static constexpr int RRB = D * (int)sizeof(T);        // tiles Q, dO [BMQ][D]: row bytes
+  static constexpr int RT = BMQ * RRB;                  // bytes per tile
+  static constexpr int STAGE = 2 * RT;                  // Q, dO
   static constexpr int LSTAGE = 2 * BMQ * 4;            // lse2, delta
   static constexpr int PW = 64 * 16 * MB * (int)sizeof(T);   // P of one wave (per lane: 16 MB values)
   static constexpr int LDS = 2 * STAGE + 2 * LSTAGE + 4 * PW;
@@ -130,16 +129,17 @@ struct QIter {
 // dP = dO V^T, dS = P (dP - delta) and dK += Q^T dS, taking P from the P wave of
 // their keys through LDS. Wave w and w + 4 share a SIMD, so the exponentials of
 // one overlap the MFMAs of the other. Both kinds run the same MFMA code on
-// different tiles (rows Q or dO, columns dO^T or Q^T) and share registers.
+// different tiles (read along the rows of Q or dO, then down the rows of dO or
+// Q) and share registers.
 template <typename T, int D>
-__global__ __launch_bounds__(512, 1) void dkdv_kernel(const Args a) {
+__global__ __launch_bounds__(512, 1) __attribute__((amdgpu_num_vgpr(192))) void dkdv_kernel(const Args a) {
   using C = DkdvCfg<T, D>;
   using Op = typename V8<T>::type;
   constexpr int BNK = C::BNK, BMQ = C::BMQ, MB = C::MB, KS = C::KS, DB = C::DB, NW = C::NW;
   constexpr int sz = (int)sizeof(T);
   __shared__ __attribute__((aligned(16))) char smem[C::LDS];
-  // Stage p: Q at 0, dO at RT, Q^T at 2 RT, dO^T at 2 RT + CT. Then the two
-  // lse2 / delta stages and the P exchange buffers.
+  // Stage p: Q at 0, dO at RT. Then the two lse2 / delta stages and the P
+  // exchange buffers.
   char* const lb0 = smem + 2 * C::STAGE;
   char* const pbuf = lb0 + 2 * C::LSTAGE;
   const unsigned sbase = lds_addr(smem);
@@ -161,12 +161,9 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(const Args a) {
       reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.q) + (long long)b * a.T * rs + (long long)h * D);
   const char* const obytes =
       reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.dout) + (long long)b * a.T * rs + (long long)h * D);
-  const long long cbase = (long long)bh * D * a.q_pitch;
-  const char* const qtbytes = reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.qt) + cbase);
-  const char* const otbytes = reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.dot) + cbase);
   const char* const lbytes = reinterpret_cast<const char*>(a.lse2 + (long long)bh * a.q_pitch);
   const unsigned ldoff = (unsigned)((long long)BH * a.q_pitch * 4);   // lse2 -> delta
-  const unsigned rrow = (unsigned)(rs * sz), crow = (unsigned)((long long)a.q_pitch * sz);
+  const unsigned rrow = (unsigned)(rs * sz);
 
   // This lane's key; a query at global position gm sees it iff s <= gm < s_hi.
   const int s = kt0 + kw * 32 + l32;
@@ -186,15 +183,13 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(const Args a) {
     for (int j = 0; j < 16; ++j) acc[db][j] = 0.f;
   const float c2 = a.c2;
 
-  // Copy one query tile (rows, columns, lse2 / delta) into stage p; the 8
+  // Copy one query tile (Q and dO rows, lse2 / delta) into stage p; the 8
   // waves share the instructions.
   auto dma_stage = [&](int p, const QIter& q) {
     const unsigned st = sbase + (unsigned)(p * C::STAGE);
     const int r0 = q.row0(), nr = q.nrows(BMQ), p0 = geo.prow(r0);
     dma_tile<BMQ, C::RRB, C::U, NW>(st, qbytes + (long long)r0 * rrow, rrow, nr, w, lane);
     dma_tile<BMQ, C::RRB, C::U, NW>(st + C::RT, obytes + (long long)r0 * rrow, rrow, nr, w, lane);
-    dma_tile<D, C::CRB, C::U, NW>(st + 2 * C::RT, qtbytes + (long long)p0 * sz, crow, D, w, lane);
-    dma_tile<D, C::CRB, C::U, NW>(st + 2 * C::RT + C::CT, otbytes + (long long)p0 * sz, crow, D, w, lane);
     if (w == 0 && lane < BMQ / 2) {
       const unsigned voff = lane < BMQ / 4 ? 16u * lane : ldoff + 16u * (lane - BMQ / 4);
       lds_dma16(lbytes + (long long)p0 * 4, voff, sbase + (unsigned)(lb0 - smem) + p * C::LSTAGE);
@@ -229,6 +224,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(const Args a) {
   __syncthreads();
 
   char* const pw = pbuf + kw * C::PW;   // P of this key block, lane-major
+  const ColRead<T, C::RRB> rcol(lane);
   for (int par = 0; it.valid; par ^= 1) {
     const int cur = __builtin_amdgcn_readfirstlane(par);
     const char* const st = smem + cur * C::STAGE;
@@ -282,14 +278,14 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(const Args a) {
         ops[q] = to_op(sp[mb], j0, T());
       }
     }
-    // dV^T += dO^T P^T (P waves) or dK^T += Q^T dS^T (dS waves).
+    // dV^T += dO^T P^T (P waves) or dK^T += Q^T dS^T (dS waves), the first
+    // operand read down the rows of the dO or Q tile.
     {
-      const char* const Cc = st + 2 * C::RT + (1 - role) * C::CT;
+      const char* const Cc = st + (1 - role) * C::RT;
 #pragma unroll
       for (int ks = 0; ks < BMQ / 16; ++ks)
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
-          mfma16(lds_sw8<T, C::CRB>(Cc, 32 * db + l32, 16 * ks + 8 * g), ops[ks], acc[db]);
+        for (int db = 0; db < DB; ++db) mfma16(rcol(Cc, 16 * ks, 32 * db), ops[ks], acc[db]);
     }
     it = i1;
     if (i1.valid) i1.next(geo, BMQ);
@@ -326,9 +322,8 @@ struct DqCfg {
   static constexpr int DB = D / 32;
   static constexpr int U = 8 * (int)sizeof(T) / 16;    // 16-byte chunks per operand
   static constexpr int KRB = D * (int)sizeof(T);       // K, V rows [BN][D]: row bytes
-  static constexpr int TRB = BN * (int)sizeof(T);      // K^T [D][BN]: row bytes
-  static constexpr int KT = BN * KRB, TT = D * TRB;    // bytes per tile
-  static constexpr int STAGE = 2 * KT + TT;            // K, V, K^T
+  static constexpr int KT = BN * KRB;                  // bytes per tile
+  static constexpr int STAGE = 2 * KT;                 // K, V
   static constexpr int OSTR = D + 4;
   static constexpr int LDS_KV = 2 * STAGE;
   static constexpr int LDS_EPI = 4 * 32 * OSTR * 4;
@@ -337,7 +332,7 @@ struct DqCfg {
 };
 
 template <typename T, int D>
-__global__ __launch_bounds__(256, 2) void dq_kernel(const Args a) {
+__global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void dq_kernel(const Args a) {
   using C = DqCfg<T, D>;
   using Op = typename V8<T>::type;
   constexpr int BM = C::BM, BN = C::BN, KS = C::KS, DB = C::DB;
@@ -360,9 +355,7 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const Args a) {
       reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.k0) + (long long)b * a.k0_bs + (long long)h * D);
   const char* const vbytes =
       reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.v0) + (long long)b * a.k0_bs + (long long)h * D);
-  const char* const ktbytes =
-      reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.kt) + (long long)bh * D * a.kv_pitch);
-  const unsigned krow = (unsigned)(rs * sz), trow = (unsigned)((long long)a.kv_pitch * sz);
+  const unsigned krow = (unsigned)(rs * sz);
   // lse2 / delta rows in the padded layout; the tile lies inside one run.
   const float* lseb = a.lse2 + (long long)bh * a.q_pitch + (geo.prow(row0) - row0);
   const float* delb = a.delta + (long long)bh * a.q_pitch + (geo.prow(row0) - row0);
@@ -391,15 +384,15 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const Args a) {
     for (int j = 0; j < 16; ++j) acc[db][j] = 0.f;
   const float c2 = a.c2;
 
-  // Stage p: K rows at 0, V rows at KT, K^T at 2 KT (swizzled, direct copies).
-  // K / V rows past the end re-read the last row: those keys are masked.
+  // Stage p: K rows at 0, V rows at KT (swizzled, direct copies). K / V rows
+  // past the end re-read the last row: those keys are masked.
   auto dma_stage = [&](int p, int s0) {
     const unsigned st = sbase + (unsigned)(p * C::STAGE);
     const int nv = a.Tkv - s0 < BN ? a.Tkv - s0 : BN;
     dma_tile<BN, C::KRB, C::U>(st, kbytes + (long long)s0 * krow, krow, nv, w, lane);
     dma_tile<BN, C::KRB, C::U>(st + C::KT, vbytes + (long long)s0 * krow, krow, nv, w, lane);
-    dma_tile<D, C::TRB, C::U>(st + 2 * C::KT, ktbytes + (long long)s0 * sz, trow, D, w, lane);
   };
+  const ColRead<T, C::KRB> kcol(lane);
   auto interior = [&](const SegIter& t) {
     return t.s0 >= t.a && t.s0 + BN <= t.b && t.s0 >= lo_max && t.s0 + BN - 1 <= g_min;
   };
@@ -427,7 +420,6 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const Args a) {
     const int cur = __builtin_amdgcn_readfirstlane(par);
     const char* const Ks = smem + cur * C::STAGE;
     const char* const Vs = Ks + C::KT;
-    const char* const KTs = Ks + 2 * C::KT;
     if (i1.valid) dma_stage(cur ^ 1, i1.s0);
     // S^T and dP^T for the 32 keys: lane = query.
     f32x16 st, dpt;
@@ -450,10 +442,10 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const Args a) {
       dpt[j] = p * (dpt[j] - dq_delta);
     }
     const Op ds0 = to_op(dpt, 0, T()), ds1 = to_op(dpt, 8, T());
-    // dQ^T += K^T dS^T over the 32 keys (2 k-steps of 16).
-    // MFMA i: 32-row block i / 2 of D, k-step i % 2 over the 32 keys.
-    mfma_ring<2 * DB, 3>(
-        [&](int i) { return lds_sw8<T, C::TRB>(KTs, 32 * (i >> 1) + l32, 16 * (i & 1) + 8 * g); },
+    // dQ^T += K^T dS^T over the 32 keys (2 k-steps of 16); K^T is read down the
+    // rows of the K tile. MFMA i: 32-row block i / 2 of D, k-step i % 2.
+    mfma_ring<2 * DB, (sizeof(T) == 2 ? 3 : 1)>(
+        [&](int i) { return kcol(Ks, 16 * (i & 1), 32 * (i >> 1)); },
         [&](int i, const Op& op) { mfma16(op, (i & 1) ? ds1 : ds0, acc[i >> 1]); });
     it = i1;
     if (i1.valid) i1.next(geo, BN);
@@ -572,8 +564,6 @@ static hipError_t launch_bwd_t(const Args& a, hipStream_t st) {
   const Geo geo{a.layout, a.cp, a.rank, a.T, a.Tkv};
   const long long nrow = (long long)a.B * a.H * a.q_pitch;
   if (nrow == 0) return hipSuccess;
-  const int dt = sizeof(T) == 2 ? 0 : 1;
-  const long long qbs = (long long)a.T * a.H * D;
   hipError_t e;
   timing_mark(st);
   {
@@ -582,24 +572,15 @@ static hipError_t launch_bwd_t(const Args& a, hipStream_t st) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   timing_mark(st);
-  hipStream_t side = nullptr;
-  if ((e = side_begin(st, 0, side)) != hipSuccess) return e;
-  if ((e = launch_xpose(a.q, qbs, const_cast<void*>(a.qt), geo.qruns(), a.B, a.H, dt, D, side)) != hipSuccess)
-    return e;
-  if ((e = launch_xpose(a.dout, qbs, const_cast<void*>(a.dot), geo.qruns(), a.B, a.H, dt, D, side)) != hipSuccess)
-    return e;
-  if ((e = launch_xpose(a.k0, a.k0_bs, const_cast<void*>(a.kt), geo.kvruns(), a.B, a.H, dt, D, st)) != hipSuccess)
-    return e;
-  timing_mark(st);
   const long long nq = (long long)geo.ntiles(DqCfg<T, D>::BM) * a.B * a.H;
   if (nq > 0) {
     hipLaunchKernelGGL((dq_kernel<T, D>), dim3((unsigned)nq), dim3(256), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   timing_mark(st);
-  if ((e = side_end(st, 0)) != hipSuccess) return e;
   if (a.N > 0) {
-    if ((e = side_begin(st, 1, side)) != hipSuccess) return e;
+    hipStream_t side = nullptr;
+    if ((e = side_begin(st, 0, side)) != hipSuccess) return e;
     hipLaunchKernelGGL((diag_bwd_kernel<T, D>), dim3(kDiagGrid), dim3(256), 0, side, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
@@ -609,7 +590,7 @@ static hipError_t launch_bwd_t(const Args& a, hipStream_t st) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   timing_mark(st);
-  if (a.N > 0 && (e = side_end(st, 1)) != hipSuccess) return e;
+  if (a.N > 0 && (e = side_end(st, 0)) != hipSuccess) return e;
   timing_mark(st);
   return hipSuccess;
 }

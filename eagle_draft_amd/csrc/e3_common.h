@@ -37,18 +37,12 @@ struct Args {
   float* delta;         // rowsum(dO * O), [B, H, q_pitch] (rows at Geo::prow)
   float* lse2;          // lse * log2(e), same layout as delta (delta = lse2 + B*H*q_pitch)
   const float* dqd;     // float32 partial of dq from the dQ kernel, [B, T, H, D] (workspace)
-  const float* dqg;     // float32 diagonal part of dq, [B, T, H, D] (workspace)
   void* dq;
   void* dk0;
   void* dv0;
   void* dkd;
   void* dvd;
-  const void* vt;       // V^T of block 0 (transposed copy, see e3_xpose.hip)
-  const void* kt;       // K^T of block 0
-  const void* qt;       // Q^T of the local rows
-  const void* dot;      // dO^T of the local rows
-  int kv_pitch;         // positions per (b, h, d) row of kt / vt
-  int q_pitch;          // positions per (b, h, d) row of qt / dot
+  int q_pitch;          // positions per (b, h) row of lse2 / delta
   const int32_t* cu;    // device cu_seqlens (global document boundaries)
   int ndocs;            // <= 1: one document
   int B, T, Tkv, H, N;
@@ -58,8 +52,9 @@ struct Args {
   int layout, cp, rank;
 };
 
-// Row runs of a transposed copy: run i holds rows [src[i], src[i]+len[i]) of the
-// source at positions [dst[i], dst[i]+len[i]) of each (b, h, d) row of length pitch.
+// Row runs of the local queries: run i holds local rows [src[i], src[i]+len[i]) at
+// positions [dst[i], dst[i]+len[i]) of a padded per-(b, h) layout of `pitch`
+// positions, each run starting at a multiple of 64.
 struct XRuns {
   int n;
   int src[2], len[2], dst[2];
@@ -94,10 +89,6 @@ void timing_mark(hipStream_t st);
 hipError_t side_begin(hipStream_t main, int k, hipStream_t& side);
 hipError_t side_end(hipStream_t main, int k);
 constexpr int kDiagGrid = 256;   // persistent grid of the diagonal-gradient kernel
-
-// Writes the transposed copy of x [B, rows, H, D] (batch stride x_bs) laid out by runs.
-hipError_t launch_xpose(const void* x, long long x_bs, void* xt, const XRuns& runs, int B, int H,
-                        int dtype, int D, hipStream_t st);
 
 // ---------------------------------------------------------------------------
 // Share geometry (host and device)
@@ -185,15 +176,6 @@ struct Geo {
       p += (len + 63) / 64 * 64;
     }
     r.pitch = p;
-    return r;
-  }
-  __host__ __device__ XRuns kvruns() const {
-    XRuns r{};
-    r.n = 1;
-    r.src[0] = 0;
-    r.len[0] = Tkv;
-    r.dst[0] = 0;
-    r.pitch = (Tkv + 63) / 64 * 64;
     return r;
   }
 
@@ -498,62 +480,26 @@ struct TileLoad {
   }
 };
 
-// MFMA operand of 8 consecutive columns of row `row` of a natural tile: A[m][k]
-// with m = row, k = col..col+7 (one 16-byte LDS read for bf16).
-template <typename T>
-__device__ __forceinline__ typename V8<T>::type lds_row8(const T* tile, int stride, int row, int col) {
-  return *reinterpret_cast<const typename V8<T>::type*>(tile + row * stride + col);
-}
-
-// MFMA operand taken down the rows of a natural tile X[k][m]: the lane (m = l%32,
-// g = l/32) gets X[k0 + {4g..4g+3, 8+4g..8+4g+3}][c0 + l%32], the row order in which
-// a 32x32 accumulator holds its rows (so an accumulator slice is the other operand).
-// bf16: two ds_read_b64_tr_b16. In each 16-lane group, source lane j reads the 4
-// columns c + 4(j%4) .. +3 of row k + j/4 and lane i receives column c + i of the
-// 4 rows.
-__device__ __forceinline__ bf16x8 lds_col8(const bf16* tile, int stride, int k0, int c0, int lane) {
-  typedef short v4s __attribute__((ext_vector_type(4)));
-  typedef __attribute__((address_space(3))) v4s lv4s;
-  const int g = lane >> 5;
-  const int j = lane & 15;
-  const int col = c0 + 16 * ((lane >> 4) & 1) + 4 * (j & 3);
-  const int row = k0 + 4 * g + (j >> 2);
-  const v4s a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lv4s*)(tile + row * stride + col));
-  const v4s b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lv4s*)(tile + (row + 8) * stride + col));
-  bf16x8 r;
-  const bf16x4 ra = __builtin_bit_cast(bf16x4, a);
-  const bf16x4 rb = __builtin_bit_cast(bf16x4, b);
-  r[0] = ra[0]; r[1] = ra[1]; r[2] = ra[2]; r[3] = ra[3];
-  r[4] = rb[0]; r[5] = rb[1]; r[6] = rb[2]; r[7] = rb[3];
-  return r;
-}
-// fp32: eight scalar LDS reads (no transposing read exists for 32-bit elements).
-__device__ __forceinline__ f32x8 lds_col8(const float* tile, int stride, int k0, int c0, int lane) {
-  const int g = lane >> 5;
-  const int col = c0 + (lane & 31);
-  f32x8 r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    r[i] = tile[(k0 + 4 * g + i) * stride + col];
-    r[4 + i] = tile[(k0 + 8 + 4 * g + i) * stride + col];
-  }
-  return r;
-}
-
 // ---- swizzled LDS tiles filled by direct global->LDS loads -----------------
 // A tile of rows of RB bytes is stored unpadded; the 16-byte chunk c of row r
 // sits in chunk slot c ^ sw(r). sw is a multiple of U (16-byte chunks per MFMA
-// operand: 1 for bf16, 2 for fp32), so an operand's chunks stay adjacent. The
-// masks are the ones measured fastest on gfx950 for 16-byte reads of one
-// operand column by 32 consecutive rows (4 waves per CU: 21.7 cycles per read
-// per wave for 256-byte rows with r mod 16, against 32 with r mod 8; 17.3 for
-// 128-byte rows with r mod 8; with 8 waves per CU all three reach the LDS peak of
-// ~256 B/clk, 64-byte rows only with (r / 4) mod 4).
+// operand: 1 for bf16, 2 for fp32), so an operand's chunks stay adjacent. Tiles
+// are read two ways, and the masks serve both without bank conflicts (64 banks
+// of 4 bytes):
+//  - along a row (lds_sw8): 32 consecutive rows, one 16-byte chunk each. Any 16
+//    consecutive rows must land in 16 distinct 16-byte bank groups;
+//  - down the rows (ColRead, ds_read_b64_tr_b16): 8 rows r0 + {0..3, 4..7}
+//    (r0 = 0 mod 8), the same 4 aligned chunks each. Each group of 4 rows must
+//    cover all 16 bank groups once.
+// 256-byte rows: sw = 4 (r mod 4) + (r / 4) mod 4 (measured on gfx950, 8 waves
+// per CU: 214 B/clk for row reads, 160 for transposing reads, against 222 and
+// 62 with sw = r mod 16). 128-byte rows (two rows per 256 bytes): sw =
+// 4 ((r / 2) mod 2) + (r / 4) mod 4. 64-byte rows (row reads only): (r / 4) mod 4.
 template <int RB, int U>
 __device__ __forceinline__ int sw_mask(int r) {
   constexpr int CPR = RB / 16;
-  if constexpr (CPR >= 16) return ((r & 15) * U) & (CPR - 1);
-  else if constexpr (CPR == 8) return ((r & 7) * U) & 7;
+  if constexpr (CPR >= 16) return ((((r & 3) << 2) | ((r >> 2) & 3)) * U) & (CPR - 1);
+  else if constexpr (CPR == 8) return (((((r >> 1) & 1) << 2) | ((r >> 2) & 3)) * U) & 7;
   else return (((r >> 2) & 3) * U) & (CPR - 1);
 }
 
@@ -655,16 +601,77 @@ __device__ __forceinline__ typename V8<T>::type lds_sw8(const char* tile, int ro
                                                        16 * (c ^ sw_mask<RB, U>(row)));
 }
 
-// Row strides (elements) of LDS tiles, chosen against 4-byte bank conflicts:
-//   nat  -- tiles read only by lds_row8 (16 consecutive rows, 16 bytes each):
-//           16 bytes of padding, so the rows start 4 banks apart;
-//   col  -- tiles read only by lds_col8 (4 rows x 32 bytes per 16 lanes): bf16
-//           rows start 16 banks apart (64 bytes of padding);
-//   both -- tiles read both ways: bf16 rows start 12 banks apart.
-template <typename T, int D> struct Stride {
-  static constexpr int nat = D + 16 / (int)sizeof(T);
-  static constexpr int col = sizeof(T) == 2 ? D + 32 : D + 4;
-  static constexpr int both = sizeof(T) == 2 ? D + 24 : D + 4;
+// MFMA operand taken down the rows of a swizzled tile X[k][m] (rows of RB bytes):
+// lane (m = l%32, g = l/32) gets X[k0 + o][c0 + m] for o = 4g..4g+3, 8+4g..8+4g+3,
+// the row order in which a 32x32 accumulator holds its rows, so that an
+// accumulator slice converted to T is the other operand. k0 is a multiple of 16
+// and c0 of 32.
+// bf16: two ds_read_b64_tr_b16. In each 16-lane group (j = l%16, h = (l/16)%2),
+// source lane j reads the 4 elements c0 + 16h + 4(j%4) .. +3 of row k0 + 4g + j/4
+// (then of that row + 8), and lane j receives element c0 + 16h + j of the 4 rows.
+// The per-lane byte offsets are fixed for k0 = c0 = 0: since sw depends on r mod
+// 16 only, rows k0 + o add k0 * RB, and since the lane's chunk (c0/8 + 2h +
+// (j/2)%2) has c0/8 in bits the lane part leaves free, columns c0 + ... XOR the
+// chunk slot with c0/8.
+template <typename T, int RB>
+struct ColRead;
+
+template <int RB>
+struct ColRead<bf16, RB> {
+  unsigned o0, o1;
+  __device__ __forceinline__ explicit ColRead(int lane) {
+    const int g = lane >> 5, j = lane & 15, h = (lane >> 4) & 1;
+    const int r = 4 * g + (j >> 2), c = 2 * h + ((j >> 1) & 1), byte = 8 * (j & 1);
+    o0 = (unsigned)(r * RB + 16 * (c ^ sw_mask<RB, 1>(r)) + byte);
+    o1 = (unsigned)((r + 8) * RB + 16 * (c ^ sw_mask<RB, 1>(r + 8)) + byte);
+  }
+  // `tile` must start at a multiple of 256 bytes of LDS: then the column XOR
+  // (below 256) commutes with adding the tile address, and the row offset k0 * RB
+  // (a multiple of 256) is an immediate offset of the read.
+  __device__ __forceinline__ bf16x8 operator()(const char* tile, int k0, int c0) const {
+    typedef short v4s __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) v4s lv4s;
+    typedef __attribute__((address_space(3))) char lchar;
+    const unsigned x = 2u * (unsigned)c0;          // 16 * (c0 / 8)
+    lchar* const t = (lchar*)tile;
+    const unsigned ta = (unsigned)(unsigned long)t;
+    lchar* const pa = t + (((ta + o0) ^ x) - ta) + k0 * RB;
+    lchar* const pb = t + (((ta + o1) ^ x) - ta) + k0 * RB;
+    const v4s va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lv4s*)pa);
+    const v4s vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lv4s*)pb);
+    const short a0 = va[0], a1 = va[1], a2 = va[2], a3 = va[3];
+    const short b0 = vb[0], b1 = vb[1], b2 = vb[2], b3 = vb[3];
+    bf16x8 r;
+    r[0] = __builtin_bit_cast(bf16, a0); r[1] = __builtin_bit_cast(bf16, a1);
+    r[2] = __builtin_bit_cast(bf16, a2); r[3] = __builtin_bit_cast(bf16, a3);
+    r[4] = __builtin_bit_cast(bf16, b0); r[5] = __builtin_bit_cast(bf16, b1);
+    r[6] = __builtin_bit_cast(bf16, b2); r[7] = __builtin_bit_cast(bf16, b3);
+    return r;
+  }
+};
+
+// fp32: eight scalar LDS reads (there is no transposing read of 32-bit
+// elements), at per-lane offsets fixed for k0 = c0 = 0; c0 (a multiple of 32)
+// XORs the chunk slot with c0/4 as in the bf16 case.
+template <int RB>
+struct ColRead<float, RB> {
+  unsigned o[8];
+  __device__ __forceinline__ explicit ColRead(int lane) {
+    const int g = lane >> 5, m = lane & 31;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = (i < 4 ? 4 * g + i : 8 + 4 * g + i - 4);
+      o[i] = (unsigned)(r * RB + 16 * ((m >> 2) ^ sw_mask<RB, 2>(r)) + 4 * (m & 3));
+    }
+  }
+  __device__ __forceinline__ f32x8 operator()(const char* tile, int k0, int c0) const {
+    const unsigned x = 4u * (unsigned)c0;          // 16 * (c0 / 4)
+    const char* const base = tile + k0 * RB;
+    f32x8 r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = *reinterpret_cast<const float*>(base + (o[i] ^ x));
+    return r;
+  }
 };
 
 }  // namespace e3

@@ -24,12 +24,11 @@ struct FwdCfg {
   static constexpr int BM = 128;
   static constexpr int BN = 64;
   static constexpr int KRB = D * (int)sizeof(T);        // K tile [BN keys][D], row bytes
-  static constexpr int VRB = BN * (int)sizeof(T);       // V^T tile [D][BN keys], row bytes
   static constexpr int U = 8 * (int)sizeof(T) / 16;     // 16-byte chunks per operand
   static constexpr int OSTR = D + 4;       // fp32 staging rows of the epilogue
   static constexpr int KS = D / 16;        // MFMA k-steps over D
   static constexpr int DB = D / 32;        // 32-row blocks of O^T
-  static constexpr int KBYTES = BN * KRB, VBYTES = D * VRB;
+  static constexpr int KBYTES = BN * KRB, VBYTES = BN * KRB;   // K, V tiles [BN keys][D]
   static constexpr int LDS_KV = 2 * (KBYTES + VBYTES);
   static constexpr int LDS_EPI = 4 * 32 * OSTR * 4 + 2 * BM * 4;
   static constexpr int LDS = LDS_KV > LDS_EPI ? LDS_KV : LDS_EPI;
@@ -56,7 +55,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const Args a) {
   const long long rs = (long long)a.H * D;
   const T* qb = reinterpret_cast<const T*>(a.q) + (long long)b * a.T * rs + (long long)h * D;
   const T* k0b = reinterpret_cast<const T*>(a.k0) + (long long)b * a.k0_bs + (long long)h * D;
-  const T* vtb = reinterpret_cast<const T*>(a.vt) + ((long long)b * a.H + h) * D * a.kv_pitch;
+  const T* vb = reinterpret_cast<const T*>(a.v0) + (long long)b * a.k0_bs + (long long)h * D;
 
   // This lane's query row.
   const int qr = w * 32 + l32;
@@ -81,7 +80,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const Args a) {
   float m_i = kNegInf, l_i = 0.f;
   const float c2 = a.c2;
 
-  // LDS: two K stages, then two V^T stages, swizzled, filled by direct loads.
+  // LDS: two K stages, then two V stages, swizzled, filled by direct loads.
   // (pointers for the reads, LDS byte addresses for the copies)
   char* const kb0 = smem;
   char* const kb1 = kb0 + C::KBYTES;
@@ -90,18 +89,19 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const Args a) {
   const unsigned sbase = lds_addr(smem);
   auto la = [&](const char* p) { return sbase + (unsigned)(p - smem); };
   const char* const kbase = reinterpret_cast<const char*>(k0b);
-  const char* const vbase = reinterpret_cast<const char*>(vtb);
+  const char* const vbase = reinterpret_cast<const char*>(vb);
   const unsigned krow = (unsigned)(rs * (long long)sizeof(T));
-  const unsigned vrow = (unsigned)(a.kv_pitch * (long long)sizeof(T));
-  // K rows past the end re-read the last row: those keys are masked.
+  // K / V rows past the end re-read the last row: those keys are masked.
   auto dma_k = [&](char* dst, int s0) {
     const int nv = a.Tkv - s0 < BN ? a.Tkv - s0 : BN;
     dma_tile<BN, C::KRB, C::U>(la(dst), kbase + (long long)s0 * krow, krow, nv, w, lane);
   };
-  // V^T rows are the D columns; the copy is zero padded to 64 positions.
   auto dma_v = [&](char* dst, int s0) {
-    dma_tile<D, C::VRB, C::U>(la(dst), vbase + (long long)s0 * (long long)sizeof(T), vrow, D, w, lane);
+    const int nv = a.Tkv - s0 < BN ? a.Tkv - s0 : BN;
+    dma_tile<BN, C::KRB, C::U>(la(dst), vbase + (long long)s0 * krow, krow, nv, w, lane);
   };
+  // V^T operands are read down the rows of the V tile.
+  const ColRead<T, C::KRB> vcol(lane);
 
   // S^T = K Q^T for 64 keys: two 32-key accumulator chains, lane = query.
   auto qk = [&](const char* Ks, f32x16 (&st)[2]) {
@@ -189,17 +189,17 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const Args a) {
     // Copies of K(j+2) and V^T(j+1), one instruction at a time between the
     // phase A MFMAs (a missing tile re-copies the current one into the free
     // stage, so the sequence has no branches).
-    constexpr int NKI = DmaShape<BN, C::KRB>::NI, NVI = DmaShape<D, C::VRB>::NI;
+    constexpr int NKI = DmaShape<BN, C::KRB>::NI, NVI = DmaShape<BN, C::KRB>::NI;
     constexpr int NDMA = NKI + NVI;
     const int dk0 = i2.valid ? i2.s0 : it.s0, dv0 = i1.valid ? i1.s0 : it.s0;
     const int dnv = a.Tkv - dk0 < BN ? a.Tkv - dk0 : BN;
+    const int vnv = a.Tkv - dv0 < BN ? a.Tkv - dv0 : BN;
     const unsigned lkw = la(Kw), lvw = la(Vw);
     auto dma_part = [&](int k) {
       if (k < NKI)
         dma_tile_part<BN, C::KRB, C::U>(lkw, kbase + (long long)dk0 * krow, krow, dnv, w, lane, k);
       else
-        dma_tile_part<D, C::VRB, C::U>(lvw, vbase + (long long)dv0 * (long long)sizeof(T), vrow, D, w,
-                                       lane, k - NKI);
+        dma_tile_part<BN, C::KRB, C::U>(lvw, vbase + (long long)dv0 * krow, krow, vnv, w, lane, k - NKI);
     };
     // Phase A: S^T(j+1) on MFMA (stale LDS when there is no tile j+1: the
     // result is then never used); P(j) and its row sum on VALU. The order is
@@ -250,13 +250,13 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const Args a) {
     {
       Op va[2][DB];
 #pragma unroll
-      for (int db = 0; db < DB; ++db) va[0][db] = lds_sw8<T, C::VRB>(Vc, 32 * db + l32, 8 * g);
+      for (int db = 0; db < DB; ++db) va[0][db] = vcol(Vc, 0, 32 * db);
 #pragma unroll
       for (int ks = 0; ks < BN / 16; ++ks) {
         if (ks + 1 < BN / 16) {
 #pragma unroll
           for (int db = 0; db < DB; ++db)
-            va[(ks + 1) & 1][db] = lds_sw8<T, C::VRB>(Vc, 32 * db + l32, 16 * (ks + 1) + 8 * g);
+            va[(ks + 1) & 1][db] = vcol(Vc, 16 * (ks + 1), 32 * db);
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -388,10 +388,6 @@ static hipError_t launch_fwd_t(const Args& a, hipStream_t st) {
   const Geo geo{a.layout, a.cp, a.rank, a.T, a.Tkv};
   const long long nt = (long long)geo.ntiles(FwdCfg<T, D>::BM) * a.B * a.H;
   if (nt == 0) return hipSuccess;
-  timing_mark(st);
-  hipError_t e = launch_xpose(a.v0, a.k0_bs, const_cast<void*>(a.vt), geo.kvruns(), a.B, a.H,
-                              sizeof(T) == 2 ? 0 : 1, D, st);
-  if (e != hipSuccess) return e;
   timing_mark(st);
   hipLaunchKernelGGL((fwd_kernel<T, D>), dim3((unsigned)nt), dim3(256), 0, st, a);
   timing_mark(st);

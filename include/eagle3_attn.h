@@ -31,7 +31,8 @@
  *     `cached_ulysses_attention`); all merging is done in float32.
  *   - Every pointer passed to a compute entry point is a DEVICE pointer unless named
  *     *_host. The caller owns (allocates and frees) every buffer, including the
- *     workspaces. The library allocates no device memory and keeps no per-call state.
+ *     backward's workspace. The library allocates no device memory and keeps no
+ *     per-call state.
  *   - Calls are asynchronous on the given HIP stream and never synchronise. The backward
  *     forks part of its work (the diagonal-block gradients) onto a side stream that
  *     waits for the given stream and is joined back into it before the call's last
@@ -76,7 +77,7 @@
 extern "C" {
 #endif
 
-#define EAGLE3_ABI_VERSION 2
+#define EAGLE3_ABI_VERSION 3
 
 typedef enum { E3_OK = 0, E3_EINVAL = -1, E3_EUNSUPPORTED = -2, E3_EHIP = -3 } e3_status;
 typedef enum { E3_BF16 = 0, E3_F32 = 1 } e3_dtype;
@@ -116,24 +117,17 @@ int eagle3_abi_version(void);
 const char* eagle3_last_error(void);
 
 /* Bytes of device workspace eagle3_attn_bwd / eagle3_shard_bwd need: delta = rowsum(dO*O)
- * and lse*log2(e) (float32 [B, H, P]), transposed copies of q and dout (dtype
- * [B, H, D, P]), P = T with each local run (the two zig-zag chunks) padded to a multiple
- * of 64 positions, and a transposed copy of k0 (dtype [B, H, D, P_kv], P_kv = T_kv
- * rounded up to 64). 0 when T == 0. Returns 0 and sets the last error for an invalid
- * problem. */
+ * and lse*log2(e) (float32 [B, H, P], P = T with each local run, i.e. each of the two
+ * zig-zag chunks, padded to a multiple of 64 positions), then, when num_blocks > 1, the
+ * block-0 part of dq (float32 [B, T, H, D]). 0 when T == 0. Returns 0 and sets the last
+ * error for an invalid problem. */
 size_t eagle3_bwd_workspace_bytes(const e3_problem* p);
-
-/* Bytes of device workspace the forward needs: a transposed copy of v0 (dtype
- * [B, H, D, P], P = T_kv rounded up to 64). 0 when T == 0. */
-size_t eagle3_fwd_workspace_bytes(const e3_problem* p);
 
 /* Forward of the full sequence (layout FULL or HEADSHARD):
  *   out [B,T,H,D] (dtype) = the joint-softmax output, lse [B,H,T] float32 = the merged
- *   log-sum-exp. kd/vd may be NULL when num_blocks == 1. workspace must hold
- *   eagle3_fwd_workspace_bytes(p) bytes, 256-byte aligned; its contents are scratch. */
+ *   log-sum-exp. kd/vd may be NULL when num_blocks == 1. No workspace. */
 int eagle3_attn_fwd(const e3_problem* p, const void* q, const void* k0, const void* v0,
-                    const void* kd, const void* vd, void* out, float* lse, void* workspace,
-                    hipStream_t stream);
+                    const void* kd, const void* vd, void* out, float* lse, hipStream_t stream);
 
 /* Backward of the full sequence (layout FULL or HEADSHARD) against the MERGED out/lse
  * produced by the forward: writes dq [B,T,H,D], dk0/dv0 [B,T_kv,H,D], dkd/dvd
@@ -149,8 +143,7 @@ int eagle3_attn_bwd(const e3_problem* p, const void* dout, const void* q, const 
  * them with the diagonals in one pass, with no inter-GPU communication. Arguments as
  * eagle3_attn_fwd / eagle3_attn_bwd. */
 int eagle3_shard_fwd(const e3_problem* p, const void* q, const void* k0, const void* v0,
-                     const void* kd, const void* vd, void* out, float* lse, void* workspace,
-                     hipStream_t stream);
+                     const void* kd, const void* vd, void* out, float* lse, hipStream_t stream);
 int eagle3_shard_bwd(const e3_problem* p, const void* dout, const void* q, const void* k0,
                      const void* v0, const void* kd, const void* vd, const void* out,
                      const float* lse, void* workspace, void* dq, void* dk0, void* dv0,
@@ -176,10 +169,10 @@ int lse_merge(float* out, float* lse, const float* block_out, const float* block
 
 /* While `events` is non-NULL, every compute entry point called on this thread records
  * events[0] on its stream before its first kernel and events[k+1] after its k-th stage
- * (at most `capacity` events; the forward has 2 stages: the V transpose and the
- * attention kernel; the backward 5: delta and lse*log2(e), the K transpose, dQ,
- * dK/dV, and the wait for the side stream's diagonal-block gradients). The caller creates and owns the events; NULL stops recording. Returns
- * E3_OK. */
+ * (at most `capacity` events; the forward has 1 stage, the attention kernel; the
+ * backward 4: delta and lse*log2(e), dQ, dK/dV, and the wait for the side stream's
+ * diagonal-block gradients). The caller creates and owns the events; NULL stops
+ * recording. Returns E3_OK. */
 int eagle3_set_timing_events(hipEvent_t* events, int capacity);
 
 /* Number of events recorded by the last compute entry point called on this thread. */

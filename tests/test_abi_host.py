@@ -63,30 +63,31 @@ def test_invalid_problems_are_rejected_before_launch(kw, code, msg):
     p = prob(**kw)
     lib = e3.lib()
     fake = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
-    rc = lib.eagle3_shard_fwd(p.ref(), fake, fake, fake, fake, fake, fake, fake, fake, None)
+    rc = lib.eagle3_shard_fwd(p.ref(), fake, fake, fake, fake, fake, fake, fake, None)
     assert rc == code
     assert msg in lib.eagle3_last_error().decode()
     rc = lib.eagle3_shard_bwd(p.ref(), *([fake] * 14), None)
     assert rc == code
     assert lib.eagle3_bwd_workspace_bytes(p.ref()) == 0
-    assert lib.eagle3_fwd_workspace_bytes(p.ref()) == 0
 
 
 def test_null_and_misaligned_pointers_are_rejected():
     lib = e3.lib()
     p = prob()
     a = ctypes.c_void_p(0x1000)
-    rc = lib.eagle3_attn_fwd(p.ref(), None, a, a, a, a, a, a, a, None)
+    rc = lib.eagle3_attn_fwd(p.ref(), None, a, a, a, a, a, a, None)
     assert rc == e3.E3_EINVAL and "q is NULL" in lib.eagle3_last_error().decode()
-    rc = lib.eagle3_attn_fwd(p.ref(), a, a, a, a, a, a, a, None, None)
-    assert rc == e3.E3_EINVAL and "workspace is NULL" in lib.eagle3_last_error().decode()
-    rc = lib.eagle3_attn_fwd(p.ref(), a, a, a, ctypes.c_void_p(0x1008), a, a, a, a, None)
+    rc = lib.eagle3_attn_fwd(p.ref(), a, a, a, a, a, a, None, None)
+    assert rc == e3.E3_EINVAL and "lse is NULL" in lib.eagle3_last_error().decode()
+    rc = lib.eagle3_attn_fwd(p.ref(), a, a, a, ctypes.c_void_p(0x1008), a, a, a, None)
     assert rc == e3.E3_EINVAL and "kd is not 16-byte aligned" in lib.eagle3_last_error().decode()
+    rc = lib.eagle3_attn_bwd(p.ref(), *([a] * 8), None, *([a] * 5), None)
+    assert rc == e3.E3_EINVAL and "workspace is NULL" in lib.eagle3_last_error().decode()
     rc = lib.eagle3_attn_bwd(p.ref(), *([a] * 13), None, None)
     assert rc == e3.E3_EINVAL and "dvd is NULL" in lib.eagle3_last_error().decode()
     # the full-sequence entry points refuse a ring share
     q = prob(layout="zigzag", cp=2, T=256, T_kv=512)
-    rc = lib.eagle3_attn_fwd(q.ref(), *([a] * 8), None)
+    rc = lib.eagle3_attn_fwd(q.ref(), *([a] * 7), None)
     assert rc == e3.E3_EINVAL and "eagle3_shard_fwd" in lib.eagle3_last_error().decode()
     # lse_merge shape checks
     rc = lib.lse_merge(a, a, a, a, 1, 4, 2, 6, 0, None)
@@ -95,27 +96,22 @@ def test_null_and_misaligned_pointers_are_rejected():
     assert rc == e3.E3_EINVAL
     # an empty problem is a valid no-op
     z = prob(T=0, T_kv=0)
-    assert lib.eagle3_attn_fwd(z.ref(), *([None] * 8), None) == e3.E3_OK
+    assert lib.eagle3_attn_fwd(z.ref(), *([None] * 7), None) == e3.E3_OK
     assert lib.eagle3_attn_bwd(z.ref(), *([None] * 14), None) == e3.E3_OK
     assert lib.lse_merge(None, None, None, None, 1, 0, 2, 8, 0, None) == e3.E3_OK
 
 
 def test_workspace_bytes():
     p = prob(B=1, T=1000, T_kv=1000, H=3)
-    # backward: lse2 and delta (float32 [B, H, P]), transposed q and dout (bf16
-    # [B, H, D, P]), P = T rounded up to 64 (one run), and transposed k0 (bf16
-    # [B, H, D, P_kv], P_kv = T_kv rounded up to 64)
+    # backward: lse2 and delta (float32 [B, H, P]), P = T rounded up to 64 (one run),
+    # and, with diagonal blocks, the block-0 part of dq (float32 [B, T, H, D])
     P = 1024
-    # and, with diagonal blocks, the diagonal part of dq (float32 [B, T, H, D])
-    assert p.workspace_bytes() == (2 * 1 * 3 * P * 4 + 2 * 1 * 3 * 128 * P * 2 + 1 * 3 * 128 * P * 2
-                                   + 1 * 1000 * 3 * 128 * 4)
+    assert p.workspace_bytes() == 2 * 1 * 3 * P * 4 + 1 * 1000 * 3 * 128 * 4
+    assert prob(B=1, T=1000, T_kv=1000, H=3, num_blocks=1).workspace_bytes() == 2 * 3 * P * 4
     # zig-zag: each of the two local chunks is padded to 64 rows on its own
     zz = e3.Problem(1, 300, 3 * 300, 3, 128, 3, 0.1, layout="zigzag", cp=3, rank=2)
-    Pz, Pkv = 2 * 192, 960
-    assert zz.workspace_bytes() == (2 * 3 * Pz * 4 + 2 * 3 * 128 * Pz * 2 + 3 * 128 * Pkv * 2
-                                    + 300 * 3 * 128 * 4)
-    # transposed v0: [B, H, D, T_kv rounded up to 64], bf16
-    assert p.fwd_workspace_bytes() == ((1 * 3 * 128 * 1024 * 2 + 255) // 256) * 256
+    Pz = 2 * 192
+    assert zz.workspace_bytes() == 2 * 3 * Pz * 4 + 300 * 3 * 128 * 4
 
 
 SHARES = [

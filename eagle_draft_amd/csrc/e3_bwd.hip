@@ -132,7 +132,7 @@ struct QIter {
 // different tiles (read along the rows of Q or dO, then down the rows of dO or
 // Q) and share registers.
 template <typename T, int D>
-__global__ __launch_bounds__(512, 1) __attribute__((amdgpu_num_vgpr(192))) void dkdv_kernel(const Args a) {
+__global__ __launch_bounds__(512, 1) void dkdv_kernel(const Args a) {
   using C = DkdvCfg<T, D>;
   using Op = typename V8<T>::type;
   constexpr int BNK = C::BNK, BMQ = C::BMQ, MB = C::MB, KS = C::KS, DB = C::DB, NW = C::NW;
@@ -239,11 +239,10 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_num_vgpr(192))) void 
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int j = 0; j < 16; ++j) sp[mb][j] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-          mfma16(lds_sw8<T, C::RRB>(R, 32 * mb + l32, 16 * ks + 8 * g), kv[ks], sp[mb]);
+      // MFMA i = ks * MB + mb, operands read three ahead.
+      mfma_ring<KS * MB, 3>(
+          [&](int i) { return lds_sw8<T, C::RRB>(R, 32 * (i % MB) + l32, 16 * (i / MB) + 8 * g); },
+          [&](int i, const Op& op) { mfma16(op, kv[i / MB], sp[i % MB]); });
     }
     Op ops[BMQ / 16];
     if (role == 0) {

@@ -31,9 +31,9 @@ if ROOT not in sys.path:
 METRIC = "EAGLE-3 mixed attn fwd+bwd TFLOP/s (causal) + % bf16 MFMA peak, T=4096 H=32 D=128"
 PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}   # MI355X dense MFMA (bf16) / fp32 vector
 PEAK_GBS = 8000.0                               # MI355X HBM3E
-KERNELS = ["fwd", "delta", "dq", "dkdv", "diag_tail"]
+KERNELS = ["fwd", "dq", "dkdv", "diag_tail"]
 FWD_STAGES = ["fwd"]
-BWD_STAGES = ["delta", "dq", "dkdv", "diag_tail"]
+BWD_STAGES = ["dq", "dkdv", "diag_tail"]
 
 
 def log(msg):
@@ -89,14 +89,12 @@ def kernel_work(w, P0):
     return {
         # q, k0, v0, kd, vd read; out, lse written
         "fwd": dict(flop=4 * pf, diag_flop=4 * diagf, bytes=u + 2 * ukv + 2 * N * u + u + rowf),
-        # dO, O, lse read; delta and lse*log2(e) written
-        "delta": dict(flop=0, diag_flop=0, bytes=2 * u + 3 * rowf),
         # q, dO, k0, v0, lse, delta read; dk0, dv0 written; S, dP, dV, dK = 4 GEMMs
         # (the diagonal-gradient kernel runs alongside on the side stream)
         "dkdv": dict(flop=8 * pf, diag_flop=0, bytes=2 * u + 4 * ukv + 2 * rowf),
-        # q, dO, k0, v0, lse, delta read; dq (or its float32 partial) written;
-        # S, dP, dQ = 3 GEMMs
-        "dq": dict(flop=6 * pf, diag_flop=0, bytes=3 * u + 2 * ukv + 2 * rowf),
+        # q, dO, O, k0, v0, lse read; delta, lse*log2(e) and dq (or its float32
+        # partial) written; S, dP, dQ = 3 GEMMs
+        "dq": dict(flop=6 * pf, diag_flop=0, bytes=3 * u + (2 if N else 1) * u + 2 * ukv + 3 * rowf),
         # wait for the diagonal gradients: q, dO, kd, vd, dq partial read;
         # dq, dkd, dvd written (the part of that kernel not hidden under dK/dV)
         "diag_tail": dict(flop=0, diag_flop=10 * diagf, bytes=2 * u + 4 * N * u + 3 * u),

@@ -7,8 +7,6 @@
 // blocks, and the diagonal gradients follow in closed form.
 //
 // Kernels, no atomics (every output element has one writer):
-//   delta_kernel  delta[b,h,t] = <dO_t, O_t> (O = the stored merged out) and
-//                 lse2 = lse * log2(e), in the 64-aligned per-run row layout
 //   dkdv_kernel   one workgroup per 128 block-0 keys (lane = key); loops over
 //                 the query tiles that see them:
 //                   S = Q K^T, P, dP = dO V^T, dS = P (dP - delta),
@@ -23,46 +21,16 @@
 //                 ds = pi (dpi - delta): dkd = scale ds q, dvd = pi dO, and
 //                 dq = (float32 partial from dQ) + scale sum_i ds_i kd_i
 //   dq_kernel     one workgroup per 128 query rows (lane = query, as in the
-//                 forward); loops over the visible 32-key tiles in ring order
+//                 forward); first writes delta[b,h,t] = <dO_t, O_t> (O = the
+//                 stored merged out) and lse2 = lse * log2(e) of its rows in the
+//                 64-aligned per-run row layout; then loops over the visible
+//                 32-key tiles in ring order
 //                 (K and V staged in swizzled LDS by direct copies; K^T read
 //                 down the K tile): dQ += dS K (float32 partial when there are
 //                 diagonals).
 #include "e3_common.h"
 
 namespace e3 {
-
-// ---------------------------------------------------------------------------
-// delta = rowsum(dO * O), lse2 = lse * log2(e); one row per LPR lanes, rows in
-// the padded layout [b][h][p] (padding positions get 0)
-// ---------------------------------------------------------------------------
-template <typename T, int D>
-__global__ __launch_bounds__(256) void delta_kernel(const Args a) {
-  constexpr int LPR = D / 8;
-  constexpr int RPB = 256 / LPR;   // rows per block
-  const Geo geo{a.layout, a.cp, a.rank, a.T, a.Tkv};
-  const int lane = threadIdx.x;
-  const int qp = a.q_pitch;
-  const long long r = (long long)blockIdx.x * RPB + lane / LPR;   // over B*H*qp
-  const long long nrow = (long long)a.B * a.H * qp;
-  const bool valid = r < nrow;
-  const long long rr = valid ? r : 0;
-  const int bh = (int)(rr / qp), p = (int)(rr % qp), b = bh / a.H, h = bh % a.H;
-  const int t = geo.trow(p);
-  const int cc = (lane % LPR) * 8;
-  float d = 0.f;
-  if (t >= 0) {
-    const long long off = (((long long)b * a.T + t) * a.H + h) * D + cc;
-    const f32x8 x = load8f(reinterpret_cast<const T*>(a.dout) + off);
-    const f32x8 y = load8f(reinterpret_cast<const T*>(a.o_in) + off);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) d += x[e] * y[e];
-  }
-  d = group_sum<LPR>(d);
-  if (valid && (lane % LPR) == 0) {
-    a.delta[rr] = d;
-    a.lse2[rr] = t >= 0 ? a.lse_in[(long long)bh * a.T + t] * kLog2e : 0.f;
-  }
-}
 
 // ---------------------------------------------------------------------------
 // dK0 / dV0
@@ -355,9 +323,9 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void dq_kernel(const A
   const char* const vbytes =
       reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.v0) + (long long)b * a.k0_bs + (long long)h * D);
   const unsigned krow = (unsigned)(rs * sz);
-  // lse2 / delta rows in the padded layout; the tile lies inside one run.
-  const float* lseb = a.lse2 + (long long)bh * a.q_pitch + (geo.prow(row0) - row0);
-  const float* delb = a.delta + (long long)bh * a.q_pitch + (geo.prow(row0) - row0);
+  // lse2 / delta of the tile's rows in the padded layout (the tile lies inside
+  // one run, which starts at a multiple of 64 positions).
+  const long long prow0 = (long long)bh * a.q_pitch + geo.prow(row0);
 
   const int qr = w * 32 + l32;
   const bool qvalid = qr < nrows;
@@ -366,15 +334,28 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void dq_kernel(const A
   const int g_min = gpos0, g_max = gpos0 + nrows - 1;
   const int lo_min = doc_lo_of(a.cu, a.ndocs, g_min);
   const int lo_max = doc_lo_of(a.cu, a.ndocs, g_max);
-  const float lq = qvalid ? lseb[row0 + qr] : 0.f;
-  const float dq_delta = qvalid ? delb[row0 + qr] : 0.f;
 
+  // This lane's half of its query row (columns 16 ks + 8 g .. + 7) of q and dO;
+  // delta = <dO, O> with O the merged forward output (each lane sums its half,
+  // one exchange with lane ^ 32 adds the other), lse2 = lse * log2(e). Both are
+  // written to the workspace for the dK/dV and diagonal-gradient kernels; the
+  // positions of the padded layout past the run's end get 0.
   Op qreg[KS], oreg[KS];
+  float dpart = 0.f;
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     const long long off = (long long)(row0 + qr) * rs + 16 * ks + 8 * g;
     qreg[ks] = qvalid ? load8(qb + off) : zero8<T>();
     oreg[ks] = qvalid ? load8(dob + off) : zero8<T>();
+    const Op ov = qvalid ? load8(reinterpret_cast<const T*>(a.o_in) + (long long)b * a.T * rs + (long long)h * D + off)
+                         : zero8<T>();
+    dpart = dot8(oreg[ks], ov, dpart);
+  }
+  const float dq_delta = swap32_sum(dpart);
+  const float lq = qvalid ? a.lse_in[(long long)bh * a.T + row0 + qr] * kLog2e : 0.f;
+  if (g == 0 && qr < ((nrows + 63) & ~63)) {
+    a.lse2[prow0 + qr] = lq;
+    a.delta[prow0 + qr] = dq_delta;
   }
   f32x16 acc[DB];
 #pragma unroll
@@ -564,12 +545,6 @@ static hipError_t launch_bwd_t(const Args& a, hipStream_t st) {
   const long long nrow = (long long)a.B * a.H * a.q_pitch;
   if (nrow == 0) return hipSuccess;
   hipError_t e;
-  timing_mark(st);
-  {
-    const long long nb = (nrow + (256 / (D / 8)) - 1) / (256 / (D / 8));
-    hipLaunchKernelGGL((delta_kernel<T, D>), dim3((unsigned)nb), dim3(256), 0, st, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
   timing_mark(st);
   const long long nq = (long long)geo.ntiles(DqCfg<T, D>::BM) * a.B * a.H;
   if (nq > 0) {

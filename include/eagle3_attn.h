@@ -170,8 +170,8 @@ int lse_merge(float* out, float* lse, const float* block_out, const float* block
 /* While `events` is non-NULL, every compute entry point called on this thread records
  * events[0] on its stream before its first kernel and events[k+1] after its k-th stage
  * (at most `capacity` events; the forward has 1 stage, the attention kernel; the
- * backward 4: delta and lse*log2(e), dQ, dK/dV, and the wait for the side stream's
- * diagonal-block gradients). The caller creates and owns the events; NULL stops
+ * backward 3: dQ (which also writes delta and lse*log2(e)), dK/dV, and the wait for the
+ * side stream's diagonal-block gradients). The caller creates and owns the events; NULL stops
  * recording. Returns E3_OK. */
 int eagle3_set_timing_events(hipEvent_t* events, int capacity);
 

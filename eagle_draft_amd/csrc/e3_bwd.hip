@@ -284,7 +284,8 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(const Args a) {
 template <typename T, int D>
 struct DqCfg {
   static constexpr int BM = 128;        // query rows per workgroup (32 per wave)
-  static constexpr int BN = 32;         // keys per step
+  static constexpr int BN = sizeof(T) == 2 ? 64 : 32;   // keys per step
+  static constexpr int KB = BN / 32;    // 32-key blocks per step
   static constexpr int KS = D / 16;
   static constexpr int DB = D / 32;
   static constexpr int U = 8 * (int)sizeof(T) / 16;    // 16-byte chunks per operand
@@ -302,7 +303,7 @@ template <typename T, int D>
 __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void dq_kernel(const Args a) {
   using C = DqCfg<T, D>;
   using Op = typename V8<T>::type;
-  constexpr int BM = C::BM, BN = C::BN, KS = C::KS, DB = C::DB;
+  constexpr int BM = C::BM, BN = C::BN, KB = C::KB, KS = C::KS, DB = C::DB;
   constexpr int sz = (int)sizeof(T);
   __shared__ __attribute__((aligned(16))) char smem[C::LDS];
   const unsigned sbase = lds_addr(smem);
@@ -376,16 +377,18 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void dq_kernel(const A
   auto interior = [&](const SegIter& t) {
     return t.s0 >= t.a && t.s0 + BN <= t.b && t.s0 >= lo_max && t.s0 + BN - 1 <= g_min;
   };
-  // Key s = t.s0 + 4g + o (o = 8(j/4) + j%4) is visible when lo <= o <= hi.
-  auto mask = [&](f32x16& st, const SegIter& t) {
+  // Key s = t.s0 + 4g + o (o = 32 kb + 8(j/4) + j%4) is visible when lo <= o <= hi.
+  auto mask = [&](f32x16 (&st)[KB], const SegIter& t) {
     const int base = t.s0 + 4 * g;
     const int lo = (t.a > loq ? t.a : loq) - base;
     const int hi = ((t.b - 1) < gq ? (t.b - 1) : gq) - base;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int o = 8 * (j >> 2) + (j & 3);
-      st[j] = (o >= lo && o <= hi) ? st[j] : kNegInf;
-    }
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int o = 32 * kb + 8 * (j >> 2) + (j & 3);
+        st[kb][j] = (o >= lo && o <= hi) ? st[kb][j] : kNegInf;
+      }
   };
 
   SegIter it, i1;
@@ -401,32 +404,41 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void dq_kernel(const A
     const char* const Ks = smem + cur * C::STAGE;
     const char* const Vs = Ks + C::KT;
     if (i1.valid) dma_stage(cur ^ 1, i1.s0);
-    // S^T and dP^T for the 32 keys: lane = query.
-    f32x16 st, dpt;
+    // S^T and dP^T for the BN keys: lane = query.
+    f32x16 st[KB], dpt[KB];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      st[j] = 0.f;
-      dpt[j] = 0.f;
-    }
-    // MFMA i: k-step i / 2, S (even, rows of K) or dP (odd, rows of V).
-    mfma_ring<2 * KS, 3>(
-        [&](int i) { return lds_sw8<T, C::KRB>((i & 1) ? Vs : Ks, l32, 16 * (i >> 1) + 8 * g); },
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        st[kb][j] = 0.f;
+        dpt[kb][j] = 0.f;
+      }
+    // MFMA i: k-step i / (2 KB), 32-key block (i / 2) mod KB, S (even i, rows of
+    // K) or dP (odd i, rows of V).
+    mfma_ring<2 * KS * KB, 3>(
+        [&](int i) {
+          return lds_sw8<T, C::KRB>((i & 1) ? Vs : Ks, 32 * ((i >> 1) % KB) + l32, 16 * (i / (2 * KB)) + 8 * g);
+        },
         [&](int i, const Op& op) {
-          if (i & 1) mfma16(op, oreg[i >> 1], dpt);
-          else mfma16(op, qreg[i >> 1], st);
+          if (i & 1) mfma16(op, oreg[i / (2 * KB)], dpt[(i >> 1) % KB]);
+          else mfma16(op, qreg[i / (2 * KB)], st[(i >> 1) % KB]);
         });
     if (!interior(it)) mask(st, it);
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const float p = fast_exp2(fmaf(st[j], c2, -lq));
-      dpt[j] = p * (dpt[j] - dq_delta);
-    }
-    const Op ds0 = to_op(dpt, 0, T()), ds1 = to_op(dpt, 8, T());
-    // dQ^T += K^T dS^T over the 32 keys (2 k-steps of 16); K^T is read down the
-    // rows of the K tile. MFMA i: 32-row block i / 2 of D, k-step i % 2.
-    mfma_ring<2 * DB, (sizeof(T) == 2 ? 3 : 1)>(
-        [&](int i) { return kcol(Ks, 16 * (i & 1), 32 * (i >> 1)); },
-        [&](int i, const Op& op) { mfma16(op, (i & 1) ? ds1 : ds0, acc[i >> 1]); });
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float p = fast_exp2(fmaf(st[kb][j], c2, -lq));
+        dpt[kb][j] = p * (dpt[kb][j] - dq_delta);
+      }
+    Op ds[2 * KB];   // k-step k: keys 16 k .. 16 k + 15
+#pragma unroll
+    for (int k = 0; k < 2 * KB; ++k) ds[k] = to_op(dpt[k >> 1], 8 * (k & 1), T());
+    // dQ^T += K^T dS^T over the BN keys (2 KB k-steps of 16); K^T is read down
+    // the rows of the K tile. MFMA i: 32-row block i mod DB of D, k-step i / DB.
+    mfma_ring<2 * KB * DB, (sizeof(T) == 2 ? 3 : 1)>(
+        [&](int i) { return kcol(Ks, 16 * (i / DB), 32 * (i % DB)); },
+        [&](int i, const Op& op) { mfma16(op, ds[i / DB], acc[i % DB]); });
     it = i1;
     if (i1.valid) i1.next(geo, BN);
     wait_all();

@@ -116,6 +116,11 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(const Args a) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int role = w >> 2;   // 0: S, P, dV   1: dP, dS, dK
   const int kw = w & 3;      // 32-key block
+  // Issue priority: the P wave of a SIMD ahead of its dS wave (its exponentials
+  // gate the dS wave), both ahead of the diagonal-gradient waves that share the
+  // SIMDs (memory-bound; they fill the issue gaps).
+  if (role == 0) __builtin_amdgcn_s_setprio(2);
+  else __builtin_amdgcn_s_setprio(1);
   const int BH = a.B * a.H;
   const int kt = tile_order(blockIdx.x / BH, (a.Tkv + BNK - 1) / BNK), bh = blockIdx.x % BH,
             b = bh / a.H, h = bh % a.H;
@@ -403,6 +408,10 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void dq_kernel(const A
     const int cur = __builtin_amdgcn_readfirstlane(par);
     const char* const Ks = smem + cur * C::STAGE;
     const char* const Vs = Ks + C::KT;
+    // Alternate the issue priority every step: the two workgroups on a CU then
+    // share each SIMD's MFMA pipe evenly instead of the older one running ahead.
+    if (cur) __builtin_amdgcn_s_setprio(1);
+    else __builtin_amdgcn_s_setprio(0);
     if (i1.valid) dma_stage(cur ^ 1, i1.s0);
     // S^T and dP^T for the BN keys: lane = query.
     f32x16 st[KB], dpt[KB];

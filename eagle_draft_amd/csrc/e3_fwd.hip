@@ -184,6 +184,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const Args a) {
   __syncthreads();   // K(0) is read; the first step overwrites its stage
   const Op ones = ones8<T>();
 
+  int hi_prio = 0;
   auto step = [&](f32x16 (&sc)[2], f32x16 (&sn)[2], const char* Kn, const char* Vc, char* Kw,
                   char* Vw) {
     // Copies of K(j+2) and V^T(j+1), one instruction at a time between the
@@ -201,6 +202,13 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const Args a) {
       else
         dma_tile_part<BN, C::KRB, C::U>(lvw, vbase + (long long)dv0 * krow, krow, vnv, w, lane, k - NKI);
     };
+    // Two workgroups share a CU, one wave of each on every SIMD. At equal
+    // priority the SIMD issues for the older wave first, which then runs far
+    // ahead of its partner and leaves lone-wave tails at the end of the grid;
+    // alternating the issue priority every key tile shares the MFMA pipe.
+    if (hi_prio) __builtin_amdgcn_s_setprio(1);
+    else __builtin_amdgcn_s_setprio(0);
+    hi_prio ^= 1;
     // Phase A: S^T(j+1) on MFMA (stale LDS when there is no tile j+1: the
     // result is then never used); P(j) and its row sum on VALU. The order is
     // fixed by scheduling fences: in step i the K operand of MFMA i+2 is read,

@@ -509,6 +509,13 @@ __device__ __forceinline__ unsigned lds_addr(const void* p) {
   return (unsigned)(unsigned long)(lds_char*)p;
 }
 
+// A wave-uniform 64-bit value moved to scalar registers.
+__device__ __forceinline__ unsigned long long uniform64(unsigned long long x) {
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)x);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(x >> 32));
+  return ((unsigned long long)hi << 32) | lo;
+}
+
 // One global_load_lds_dwordx4: 16 bytes from `base` + `voff` (per lane) to LDS
 // byte `lds` + 16 * lane (lds uniform). It has no register outputs; its
 // completion is waited for with vmcnt. Written as asm because the compiler
@@ -564,6 +571,25 @@ __device__ __forceinline__ void dma_tile_part(unsigned lds, const char* base, un
     const unsigned off = (unsigned)rr * stride + 16u * (unsigned)((lane % S::CPR) ^ sw_mask<RB, U>(r));
     lds_dma16(base, off, lds + (unsigned)(r0 * RB));
   }
+}
+
+// Per-lane source offset of instruction i of this wave's share of a full-tile
+// copy (all R rows valid), relative to the tile's first row: the same for every
+// tile of a given stride, so a loop computes it once and then issues each copy
+// from a scalar tile base (no per-copy address arithmetic).
+template <int R, int RB, int U, int NW = 4>
+__device__ __forceinline__ unsigned dma_full_off(unsigned stride, int w, int lane, int i) {
+  using S = DmaShape<R, RB, NW>;
+  const int r0 = (w * S::NI + i) * S::RPI;
+  const int rl = lane / S::CPR;
+  return (unsigned)(r0 + rl) * stride + 16u * (unsigned)((lane % S::CPR) ^ sw_mask<RB, U>((r0 & 15) + rl));
+}
+
+// LDS byte offset, within the tile, of instruction i of this wave's share.
+template <int R, int RB, int NW = 4>
+__device__ __forceinline__ unsigned dma_full_lds(int w, int i) {
+  using S = DmaShape<R, RB, NW>;
+  return (unsigned)((w * S::NI + i) * S::RPI * RB);
 }
 
 template <int R, int RB, int U, int NW = 4>
@@ -639,14 +665,10 @@ struct ColRead<bf16, RB> {
     lchar* const pb = t + (((ta + o1) ^ x) - ta) + k0 * RB;
     const v4s va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lv4s*)pa);
     const v4s vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lv4s*)pb);
-    const short a0 = va[0], a1 = va[1], a2 = va[2], a3 = va[3];
-    const short b0 = vb[0], b1 = vb[1], b2 = vb[2], b3 = vb[3];
-    bf16x8 r;
-    r[0] = __builtin_bit_cast(bf16, a0); r[1] = __builtin_bit_cast(bf16, a1);
-    r[2] = __builtin_bit_cast(bf16, a2); r[3] = __builtin_bit_cast(bf16, a3);
-    r[4] = __builtin_bit_cast(bf16, b0); r[5] = __builtin_bit_cast(bf16, b1);
-    r[6] = __builtin_bit_cast(bf16, b2); r[7] = __builtin_bit_cast(bf16, b3);
-    return r;
+    // Whole-register concatenation (element-wise inserts cost a VALU op each).
+    typedef short v8s __attribute__((ext_vector_type(8)));
+    const v8s r = __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, r);
   }
 };
 

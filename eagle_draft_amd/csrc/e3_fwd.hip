@@ -91,6 +91,14 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const Args a) {
   const char* const kbase = reinterpret_cast<const char*>(k0b);
   const char* const vbase = reinterpret_cast<const char*>(vb);
   const unsigned krow = (unsigned)(rs * (long long)sizeof(T));
+  // Scalar K / V bases and the per-lane offsets of this wave's full-tile copies
+  // (the same for K and V), so a step issues each copy with no address math.
+  const unsigned long long kbs = uniform64((unsigned long long)kbase);
+  const unsigned long long vbs = uniform64((unsigned long long)vbase);
+  constexpr int NKI0 = DmaShape<BN, C::KRB>::NI;
+  unsigned dmoff[NKI0];
+#pragma unroll
+  for (int i = 0; i < NKI0; ++i) dmoff[i] = dma_full_off<BN, C::KRB, C::U>(krow, w, lane, i);
   // K / V rows past the end re-read the last row: those keys are masked.
   auto dma_k = [&](char* dst, int s0) {
     const int nv = a.Tkv - s0 < BN ? a.Tkv - s0 : BN;
@@ -196,11 +204,18 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const Args a) {
     const int dnv = a.Tkv - dk0 < BN ? a.Tkv - dk0 : BN;
     const int vnv = a.Tkv - dv0 < BN ? a.Tkv - dv0 : BN;
     const unsigned lkw = la(Kw), lvw = la(Vw);
+    const unsigned dk0s = __builtin_amdgcn_readfirstlane((unsigned)dk0);
+    const unsigned dv0s = __builtin_amdgcn_readfirstlane((unsigned)dv0);
+    const char* const ktile = (const char*)(kbs + (unsigned long long)dk0s * krow);
+    const char* const vtile = (const char*)(vbs + (unsigned long long)dv0s * krow);
     auto dma_part = [&](int k) {
-      if (k < NKI)
-        dma_tile_part<BN, C::KRB, C::U>(lkw, kbase + (long long)dk0 * krow, krow, dnv, w, lane, k);
-      else
-        dma_tile_part<BN, C::KRB, C::U>(lvw, vbase + (long long)dv0 * krow, krow, vnv, w, lane, k - NKI);
+      if (k < NKI) {
+        if (dnv >= BN) lds_dma16(ktile, dmoff[k], lkw + dma_full_lds<BN, C::KRB>(w, k));
+        else dma_tile_part<BN, C::KRB, C::U>(lkw, kbase + (long long)dk0 * krow, krow, dnv, w, lane, k);
+      } else {
+        if (vnv >= BN) lds_dma16(vtile, dmoff[k - NKI], lvw + dma_full_lds<BN, C::KRB>(w, k - NKI));
+        else dma_tile_part<BN, C::KRB, C::U>(lvw, vbase + (long long)dv0 * krow, krow, vnv, w, lane, k - NKI);
+      }
     };
     // Two workgroups share a CU, one wave of each on every SIMD. At equal
     // priority the SIMD issues for the older wave first, which then runs far

@@ -130,10 +130,10 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(const Args a) {
 
   const long long rs = (long long)a.H * D;
   const T* kvb = reinterpret_cast<const T*>(role ? a.v0 : a.k0) + (long long)b * a.k0_bs + (long long)h * D;
-  const char* const qbytes =
-      reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.q) + (long long)b * a.T * rs + (long long)h * D);
-  const char* const obytes =
-      reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.dout) + (long long)b * a.T * rs + (long long)h * D);
+  const char* const qbytes = (const char*)uniform64(
+      (unsigned long long)(reinterpret_cast<const T*>(a.q) + (long long)b * a.T * rs + (long long)h * D));
+  const char* const obytes = (const char*)uniform64(
+      (unsigned long long)(reinterpret_cast<const T*>(a.dout) + (long long)b * a.T * rs + (long long)h * D));
   const char* const lbytes = reinterpret_cast<const char*>(a.lse2 + (long long)bh * a.q_pitch);
   const unsigned ldoff = (unsigned)((long long)BH * a.q_pitch * 4);   // lse2 -> delta
   const unsigned rrow = (unsigned)(rs * sz);
@@ -158,11 +158,12 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(const Args a) {
 
   // Copy one query tile (Q and dO rows, lse2 / delta) into stage p; the 8
   // waves share the instructions.
+  const TileDma<BMQ, C::RRB, C::U, NW> tdma(rrow, w, lane);
   auto dma_stage = [&](int p, const QIter& q) {
     const unsigned st = sbase + (unsigned)(p * C::STAGE);
     const int r0 = q.row0(), nr = q.nrows(BMQ), p0 = geo.prow(r0);
-    dma_tile<BMQ, C::RRB, C::U, NW>(st, qbytes + (long long)r0 * rrow, rrow, nr, w, lane);
-    dma_tile<BMQ, C::RRB, C::U, NW>(st + C::RT, obytes + (long long)r0 * rrow, rrow, nr, w, lane);
+    tdma(st, qbytes + (long long)r0 * rrow, nr);
+    tdma(st + C::RT, obytes + (long long)r0 * rrow, nr);
     if (w == 0 && lane < BMQ / 2) {
       const unsigned voff = lane < BMQ / 4 ? 16u * lane : ldoff + 16u * (lane - BMQ / 4);
       lds_dma16(lbytes + (long long)p0 * 4, voff, sbase + (unsigned)(lb0 - smem) + p * C::LSTAGE);

@@ -600,6 +600,37 @@ __device__ __forceinline__ void dma_tile(unsigned lds, const char* base, unsigne
     dma_tile_part<R, RB, U, NW>(lds, base, stride, nvalid, w, lane, i);
 }
 
+// A wave's share of the copies of R-row tiles of one row stride. Full tiles are
+// copied from a scalar tile base with per-lane offsets computed once here (no
+// address arithmetic per copy); a partial tile takes dma_tile's clamped path.
+template <int R, int RB, int U, int NW = 4>
+struct TileDma {
+  static constexpr int NI = DmaShape<R, RB, NW>::NI;
+  unsigned off[NI];
+  unsigned stride;
+  int w, lane;
+  __device__ __forceinline__ TileDma(unsigned stride_, int w_, int lane_) : stride(stride_), w(w_), lane(lane_) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) off[i] = dma_full_off<R, RB, U, NW>(stride, w, lane, i);
+  }
+  // Copy instruction i of a full tile whose first row is at `tile` (wave-uniform,
+  // in scalar registers) to the tile at LDS byte address `lds`.
+  __device__ __forceinline__ void part(unsigned lds, const char* tile, int i) const {
+    lds_dma16(tile, off[i], lds + dma_full_lds<R, RB, NW>(w, i));
+  }
+  // The whole share of the copy of the tile at `base`; rows at or past `nvalid`
+  // re-read row nvalid - 1.
+  __device__ __forceinline__ void operator()(unsigned lds, const char* base, int nvalid) const {
+    if (nvalid >= R) {
+      const char* const tile = (const char*)uniform64((unsigned long long)base);
+#pragma unroll
+      for (int i = 0; i < NI; ++i) part(lds, tile, i);
+    } else {
+      dma_tile<R, RB, U, NW>(lds, base, stride, nvalid, w, lane);
+    }
+  }
+};
+
 // Runs the n MFMAs of a phase with their LDS operands read A steps ahead into a
 // ring, one fence per step so the compiler keeps the reads ahead:
 // `read(i)` returns operand i, `mma(i, op)` issues MFMA i.

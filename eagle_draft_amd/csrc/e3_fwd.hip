@@ -95,10 +95,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const Args a) {
   // (the same for K and V), so a step issues each copy with no address math.
   const unsigned long long kbs = uniform64((unsigned long long)kbase);
   const unsigned long long vbs = uniform64((unsigned long long)vbase);
-  constexpr int NKI0 = DmaShape<BN, C::KRB>::NI;
-  unsigned dmoff[NKI0];
-#pragma unroll
-  for (int i = 0; i < NKI0; ++i) dmoff[i] = dma_full_off<BN, C::KRB, C::U>(krow, w, lane, i);
+  const TileDma<BN, C::KRB, C::U> tdma(krow, w, lane);
   // K / V rows past the end re-read the last row: those keys are masked.
   auto dma_k = [&](char* dst, int s0) {
     const int nv = a.Tkv - s0 < BN ? a.Tkv - s0 : BN;
@@ -164,8 +161,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const Args a) {
     }
   };
 
-  // Step j: S^T(j) is in registers, K(j+1) and V^T(j) are in LDS. The step
-  // first starts the copies of K(j+2) and V^T(j+1) into the stages step j-1
+  // Step j: S^T(j) is in registers, K(j+1) and V(j) are in LDS. The step
+  // first starts the copies of K(j+2) and V(j+1) into the stages step j-1
   // finished with, then overlaps the MFMAs of S^T(j+1) with the exponentials
   // of tile j, and the MFMAs of O^T += V^T P^T for tile j with the mask and row
   // max of tile j+1.
@@ -195,9 +192,10 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const Args a) {
   int hi_prio = 0;
   auto step = [&](f32x16 (&sc)[2], f32x16 (&sn)[2], const char* Kn, const char* Vc, char* Kw,
                   char* Vw) {
-    // Copies of K(j+2) and V^T(j+1), one instruction at a time between the
-    // phase A MFMAs (a missing tile re-copies the current one into the free
-    // stage, so the sequence has no branches).
+    // Copies of K(j+2) and V(j+1) into the stages step j-1 finished with, all
+    // issued at the start of the step (a missing tile re-copies the current one
+    // into the free stage, so the sequence has no branches). Spreading them
+    // between the phase A MFMAs measured ~8% slower.
     constexpr int NKI = DmaShape<BN, C::KRB>::NI, NVI = DmaShape<BN, C::KRB>::NI;
     constexpr int NDMA = NKI + NVI;
     const int dk0 = i2.valid ? i2.s0 : it.s0, dv0 = i1.valid ? i1.s0 : it.s0;
@@ -210,10 +208,10 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const Args a) {
     const char* const vtile = (const char*)(vbs + (unsigned long long)dv0s * krow);
     auto dma_part = [&](int k) {
       if (k < NKI) {
-        if (dnv >= BN) lds_dma16(ktile, dmoff[k], lkw + dma_full_lds<BN, C::KRB>(w, k));
+        if (dnv >= BN) tdma.part(lkw, ktile, k);
         else dma_tile_part<BN, C::KRB, C::U>(lkw, kbase + (long long)dk0 * krow, krow, dnv, w, lane, k);
       } else {
-        if (vnv >= BN) lds_dma16(vtile, dmoff[k - NKI], lvw + dma_full_lds<BN, C::KRB>(w, k - NKI));
+        if (vnv >= BN) tdma.part(lvw, vtile, k - NKI);
         else dma_tile_part<BN, C::KRB, C::U>(lvw, vbase + (long long)dv0 * krow, krow, vnv, w, lane, k - NKI);
       }
     };
@@ -228,6 +226,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const Args a) {
     // result is then never used); P(j) and its row sum on VALU. The order is
     // fixed by scheduling fences: in step i the K operand of MFMA i+2 is read,
     // MFMA i issues, and 2 of the 32 exponentials of this lane are computed.
+#pragma unroll
+    for (int k = 0; k < NDMA; ++k) dma_part(k);
     const float nb = m_i == kNegInf ? 0.f : -m_i;
     Op pv[BN / 16];
     float rsum = 0.f;
@@ -245,8 +245,6 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const Args a) {
         if (i + 2 < NQ)
           ka[(i + 2) % 3] = lds_sw8<T, C::KRB>(Kn, 32 * ((i + 2) & 1) + l32, 16 * ((i + 2) >> 1) + 8 * g);
         mfma16(ka[i % 3], qreg[i >> 1], sn[i & 1]);
-#pragma unroll
-        for (int k = (NDMA * i + NQ - 1) / NQ; k < (NDMA * (i + 1) + NQ - 1) / NQ; ++k) dma_part(k);
         // Exponentials: 32 per lane over the NQ steps.
 #pragma unroll
         for (int e = (32 * i) / NQ; e < (32 * (i + 1)) / NQ; ++e)

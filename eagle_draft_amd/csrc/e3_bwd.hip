@@ -122,7 +122,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(const Args a) {
   if (role == 0) __builtin_amdgcn_s_setprio(2);
   else __builtin_amdgcn_s_setprio(1);
   const int BH = a.B * a.H;
-  const int kt = tile_order(blockIdx.x / BH, (a.Tkv + BNK - 1) / BNK), bh = blockIdx.x % BH,
+  const int kt = blockIdx.x / BH, bh = blockIdx.x % BH,
             b = bh / a.H, h = bh % a.H;
   const Geo geo{a.layout, a.cp, a.rank, a.T, a.Tkv};
   const int kt0 = kt * BNK;

@@ -61,20 +61,6 @@ struct XRuns {
   int pitch;
 };
 
-// Launch order of tiles. 0: most work first. 1: alternate the heaviest and the
-// lightest remaining tile, so that co-resident workgroups mix MFMA-heavy main
-// loops with memory-heavy epilogues.
-#ifndef E3_TILE_ORDER
-#define E3_TILE_ORDER 0
-#endif
-__host__ __device__ inline int tile_order(int o, int n) {
-#if E3_TILE_ORDER == 1
-  return (o & 1) ? n - 1 - (o >> 1) : (o >> 1);
-#else
-  (void)n;
-  return o;
-#endif
-}
 
 // Measurement hook (host): records the next caller-provided timing event, if any,
 // on the stream. Called before the first kernel of an entry point and after each.
@@ -194,7 +180,7 @@ struct Geo {
   // keys) first. Returns the local first row, the row count and the global
   // position of the first row.
   __host__ __device__ void qtile(int order, int BM, int& row0, int& nrows, int& gpos0) const {
-    int trank = tile_order(order, ntiles(BM));
+    int trank = order;
     for (int r = nruns() - 1; r >= 0; --r) {
       int ls, len, gb;
       run(r, ls, len, gb);
@@ -216,7 +202,7 @@ struct Geo {
 
 // Walks the block-0 key tiles of width BN that a query tile can see: segment by
 // segment in ring order, each segment clipped to the key window [wlo, whi).
-// Tile starts are multiples of BN (so transposed copies are read aligned); keys
+// Tile starts are multiples of BN (one tile grid per head, so the tiles are shared in L2); keys
 // of a tile outside [a, b) or outside a row's visible range are masked by the
 // kernel.
 struct SegIter {

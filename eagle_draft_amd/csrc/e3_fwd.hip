@@ -365,8 +365,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const Args a) {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           const long long off = (long long)(i0 + (i < n ? i : n - 1)) * a.kd_blk + row[u] * rs;
-          kv[u][i] = load8(kdb + off);
-          vv[u][i] = load8(vdb + off);
+          kv[u][i] = load8_nt(kdb + off);
+          vv[u][i] = load8_nt(vdb + off);
         }
 #pragma unroll
       for (int u = 0; u < 2; ++u) {

@@ -24,7 +24,7 @@
 //                 forward); first writes delta[b,h,t] = <dO_t, O_t> (O = the
 //                 stored merged out) and lse2 = lse * log2(e) of its rows in the
 //                 64-aligned per-run row layout; then loops over the visible
-//                 32-key tiles in ring order
+//                 64-key tiles (32 for float32) in ring order
 //                 (K and V staged in swizzled LDS by direct copies; K^T read
 //                 down the K tile): dQ += dS K (float32 partial when there are
 //                 diagonals).

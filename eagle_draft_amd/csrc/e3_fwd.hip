@@ -20,8 +20,9 @@ namespace e3 {
 
 template <typename T, int D>
 struct FwdCfg {
-  static constexpr int NT = 256;
-  static constexpr int BM = 128;
+  static constexpr int NW = 4;             // waves
+  static constexpr int NT = 64 * NW;
+  static constexpr int BM = 32 * NW;       // query rows per workgroup (32 per wave)
   static constexpr int BN = 64;
   static constexpr int KRB = D * (int)sizeof(T);        // K tile [BN keys][D], row bytes
   static constexpr int U = 8 * (int)sizeof(T) / 16;     // 16-byte chunks per operand
@@ -30,7 +31,7 @@ struct FwdCfg {
   static constexpr int DB = D / 32;        // 32-row blocks of O^T
   static constexpr int KBYTES = BN * KRB, VBYTES = BN * KRB;   // K, V tiles [BN keys][D]
   static constexpr int LDS_KV = 2 * (KBYTES + VBYTES);
-  static constexpr int LDS_EPI = 4 * 32 * OSTR * 4 + 2 * BM * 4;
+  static constexpr int LDS_EPI = NW * 32 * OSTR * 4 + 2 * BM * 4;
   static constexpr int LDS = LDS_KV > LDS_EPI ? LDS_KV : LDS_EPI;
   static constexpr int NB = sizeof(T) == 2 ? 8 : 2;   // diagonal blocks per epilogue group
 };
@@ -40,6 +41,7 @@ constexpr float kRescaleSlack = 8.0f;      // log2 of the largest un-rescaled gr
 template <typename T, int D>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(const Args a) {
   using C = FwdCfg<T, D>;
+  constexpr int NW = C::NW;
   using Op = typename V8<T>::type;
   constexpr int BM = C::BM, BN = C::BN, KS = C::KS, DB = C::DB;
   __shared__ __attribute__((aligned(16))) char smem[C::LDS];
@@ -88,22 +90,20 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const Args a) {
   char* const vb1 = vb0 + C::VBYTES;
   const unsigned sbase = lds_addr(smem);
   auto la = [&](const char* p) { return sbase + (unsigned)(p - smem); };
-  const char* const kbase = reinterpret_cast<const char*>(k0b);
-  const char* const vbase = reinterpret_cast<const char*>(vb);
-  const unsigned krow = (unsigned)(rs * (long long)sizeof(T));
   // Scalar K / V bases and the per-lane offsets of this wave's full-tile copies
   // (the same for K and V), so a step issues each copy with no address math.
-  const unsigned long long kbs = uniform64((unsigned long long)kbase);
-  const unsigned long long vbs = uniform64((unsigned long long)vbase);
-  const TileDma<BN, C::KRB, C::U> tdma(krow, w, lane);
+  const char* const kbase = (const char*)uniform64((unsigned long long)k0b);
+  const char* const vbase = (const char*)uniform64((unsigned long long)vb);
+  const unsigned krow = (unsigned)(rs * (long long)sizeof(T));
+  const TileDma<BN, C::KRB, C::U, NW> tdma(krow, w, lane);
   // K / V rows past the end re-read the last row: those keys are masked.
   auto dma_k = [&](char* dst, int s0) {
     const int nv = a.Tkv - s0 < BN ? a.Tkv - s0 : BN;
-    dma_tile<BN, C::KRB, C::U>(la(dst), kbase + (long long)s0 * krow, krow, nv, w, lane);
+    tdma(la(dst), kbase + (long long)s0 * krow, nv);
   };
   auto dma_v = [&](char* dst, int s0) {
     const int nv = a.Tkv - s0 < BN ? a.Tkv - s0 : BN;
-    dma_tile<BN, C::KRB, C::U>(la(dst), vbase + (long long)s0 * krow, krow, nv, w, lane);
+    tdma(la(dst), vbase + (long long)s0 * krow, nv);
   };
   // V^T operands are read down the rows of the V tile.
   const ColRead<T, C::KRB> vcol(lane);
@@ -161,11 +161,10 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const Args a) {
     }
   };
 
-  // Step j: S^T(j) is in registers, K(j+1) and V(j) are in LDS. The step
-  // first starts the copies of K(j+2) and V(j+1) into the stages step j-1
-  // finished with, then overlaps the MFMAs of S^T(j+1) with the exponentials
-  // of tile j, and the MFMAs of O^T += V^T P^T for tile j with the mask and row
-  // max of tile j+1.
+  // Step j: S^T(j) is in registers, K(j+1) and V(j) are in LDS. Phase A
+  // overlaps the MFMAs of S^T(j+1) with the exponentials of tile j; phase B
+  // the MFMAs of O^T += V^T P^T for tile j with the mask and row max of tile
+  // j+1. Tiles j, j+1, j+2 of the walk are it, i1, i2.
   SegIter it, i1, i2;
   it.begin(geo, lo_min, g_max + 1, BN);
   i1 = it;
@@ -186,117 +185,114 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const Args a) {
     if (!interior(it)) mask(sa, it);
     rescale(rowmax(sa));
   }
-  __syncthreads();   // K(0) is read; the first step overwrites its stage
+  __syncthreads();   // K(0) is read; K(2) may be copied into its stage
   const Op ones = ones8<T>();
 
-  int hi_prio = 0;
-  auto step = [&](f32x16 (&sc)[2], f32x16 (&sn)[2], const char* Kn, const char* Vc, char* Kw,
-                  char* Vw) {
-    // Copies of K(j+2) and V(j+1) into the stages step j-1 finished with, all
-    // issued at the start of the step (a missing tile re-copies the current one
-    // into the free stage, so the sequence has no branches). Spreading them
-    // between the phase A MFMAs measured ~8% slower.
-    constexpr int NKI = DmaShape<BN, C::KRB>::NI, NVI = DmaShape<BN, C::KRB>::NI;
-    constexpr int NDMA = NKI + NVI;
-    const int dk0 = i2.valid ? i2.s0 : it.s0, dv0 = i1.valid ? i1.s0 : it.s0;
-    const int dnv = a.Tkv - dk0 < BN ? a.Tkv - dk0 : BN;
-    const int vnv = a.Tkv - dv0 < BN ? a.Tkv - dv0 : BN;
-    const unsigned lkw = la(Kw), lvw = la(Vw);
-    const unsigned dk0s = __builtin_amdgcn_readfirstlane((unsigned)dk0);
-    const unsigned dv0s = __builtin_amdgcn_readfirstlane((unsigned)dv0);
-    const char* const ktile = (const char*)(kbs + (unsigned long long)dk0s * krow);
-    const char* const vtile = (const char*)(vbs + (unsigned long long)dv0s * krow);
-    auto dma_part = [&](int k) {
-      if (k < NKI) {
-        if (dnv >= BN) tdma.part(lkw, ktile, k);
-        else dma_tile_part<BN, C::KRB, C::U>(lkw, kbase + (long long)dk0 * krow, krow, dnv, w, lane, k);
-      } else {
-        if (vnv >= BN) tdma.part(lvw, vtile, k - NKI);
-        else dma_tile_part<BN, C::KRB, C::U>(lvw, vbase + (long long)dv0 * krow, krow, vnv, w, lane, k - NKI);
-      }
-    };
-    // Two workgroups share a CU, one wave of each on every SIMD. At equal
-    // priority the SIMD issues for the older wave first, which then runs far
-    // ahead of its partner and leaves lone-wave tails at the end of the grid;
-    // alternating the issue priority every key tile shares the MFMA pipe.
-    if (hi_prio) __builtin_amdgcn_s_setprio(1);
-    else __builtin_amdgcn_s_setprio(0);
-    hi_prio ^= 1;
-    // Phase A: S^T(j+1) on MFMA (stale LDS when there is no tile j+1: the
-    // result is then never used); P(j) and its row sum on VALU. The order is
-    // fixed by scheduling fences: in step i the K operand of MFMA i+2 is read,
-    // MFMA i issues, and 2 of the 32 exponentials of this lane are computed.
-#pragma unroll
-    for (int k = 0; k < NDMA; ++k) dma_part(k);
+  // This wave's share of the copy of tile t's K or V rows into a stage
+  // (nothing when the walk has no tile t).
+  auto copy_k = [&](const SegIter& t, char* dst) {
+    if (t.valid) dma_k(dst, t.s0);
+  };
+  auto copy_v = [&](const SegIter& t, char* dst) {
+    if (t.valid) dma_v(dst, t.s0);
+  };
+  Op pv[BN / 16];   // P(j) as MFMA operands, from phase A to phase B
+  // Phase A: S^T(j+1) on MFMA (stale LDS when there is no tile j+1: the
+  // result is then never used); P(j) and its row sum on VALU. The order is
+  // fixed by scheduling fences: in step i the K operand of MFMA i+2 is read,
+  // MFMA i issues, and 2 of the 32 exponentials of this lane are computed.
+  auto phase_a = [&](f32x16 (&sc)[2], f32x16 (&sn)[2], const char* Kn) {
     const float nb = m_i == kNegInf ? 0.f : -m_i;
-    Op pv[BN / 16];
     float rsum = 0.f;
-    {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) sn[kb][j] = 0.f;
-      constexpr int NQ = 2 * KS;                 // MFMAs: i = 2 ks + kb
-      Op ka[3];
-      ka[0] = lds_sw8<T, C::KRB>(Kn, l32, 8 * g);
-      ka[1] = lds_sw8<T, C::KRB>(Kn, 32 + l32, 8 * g);
+      for (int j = 0; j < 16; ++j) sn[kb][j] = 0.f;
+    constexpr int NQ = 2 * KS;                 // MFMAs: i = 2 ks + kb
+    Op ka[3];
+    ka[0] = lds_sw8<T, C::KRB>(Kn, l32, 8 * g);
+    ka[1] = lds_sw8<T, C::KRB>(Kn, 32 + l32, 8 * g);
 #pragma unroll
-      for (int i = 0; i < NQ; ++i) {
-        if (i + 2 < NQ)
-          ka[(i + 2) % 3] = lds_sw8<T, C::KRB>(Kn, 32 * ((i + 2) & 1) + l32, 16 * ((i + 2) >> 1) + 8 * g);
-        mfma16(ka[i % 3], qreg[i >> 1], sn[i & 1]);
-        // Exponentials: 32 per lane over the NQ steps.
+    for (int i = 0; i < NQ; ++i) {
+      if (i + 2 < NQ)
+        ka[(i + 2) % 3] = lds_sw8<T, C::KRB>(Kn, 32 * ((i + 2) & 1) + l32, 16 * ((i + 2) >> 1) + 8 * g);
+      mfma16(ka[i % 3], qreg[i >> 1], sn[i & 1]);
+      // Exponentials: 32 per lane over the NQ steps.
 #pragma unroll
-        for (int e = (32 * i) / NQ; e < (32 * (i + 1)) / NQ; ++e)
-          sc[e >> 4][e & 15] = fast_exp2(fmaf(sc[e >> 4][e & 15], c2, nb));
-        // Every 8 exponentials: one bf16 operand and its part of the row sum.
-        // (pinned here: otherwise they sink past the mask branch below, away
-        // from the MFMAs they overlap).
+      for (int e = (32 * i) / NQ; e < (32 * (i + 1)) / NQ; ++e)
+        sc[e >> 4][e & 15] = fast_exp2(fmaf(sc[e >> 4][e & 15], c2, nb));
+      // Every 8 exponentials: one bf16 operand and its part of the row sum.
+      // (pinned here: otherwise they sink past the mask branch below, away
+      // from the MFMAs they overlap).
 #pragma unroll
-        for (int q = 0; q < BN / 16; ++q)
-          if ((32 * (i + 1)) / NQ >= 8 * (q + 1) && (32 * i) / NQ < 8 * (q + 1)) {
-            pv[q] = to_op(sc[q >> 1], 8 * (q & 1), T());
-            rsum = dot8(pv[q], ones, rsum);
-            pin(pv[q]);
-            pin(rsum);
-          }
-        __builtin_amdgcn_sched_barrier(0);
-      }
+      for (int q = 0; q < BN / 16; ++q)
+        if ((32 * (i + 1)) / NQ >= 8 * (q + 1) && (32 * i) / NQ < 8 * (q + 1)) {
+          pv[q] = to_op(sc[q >> 1], 8 * (q & 1), T());
+          rsum = dot8(pv[q], ones, rsum);
+          pin(pv[q]);
+          pin(rsum);
+        }
+      __builtin_amdgcn_sched_barrier(0);
     }
     l_i += rsum;
     if (i1.valid && !interior(i1)) mask(sn, i1);
-    // Phase B: O^T += V^T(j) P^T(j) on MFMA, operands read one k-step ahead;
-    // the row max of tile j+1 on VALU, a quarter per k-step.
+  };
+  // Phase B: O^T += V^T(j) P^T(j) on MFMA, operands read one k-step ahead;
+  // the row max of tile j+1 on VALU, a quarter per k-step.
+  auto phase_b = [&](const f32x16 (&sn)[2], const char* Vc) {
     float mx0 = kNegInf, mx1 = kNegInf;
-    {
-      Op va[2][DB];
+    Op va[2][DB];
 #pragma unroll
-      for (int db = 0; db < DB; ++db) va[0][db] = vcol(Vc, 0, 32 * db);
+    for (int db = 0; db < DB; ++db) va[0][db] = vcol(Vc, 0, 32 * db);
 #pragma unroll
-      for (int ks = 0; ks < BN / 16; ++ks) {
-        if (ks + 1 < BN / 16) {
+    for (int ks = 0; ks < BN / 16; ++ks) {
+      if (ks + 1 < BN / 16) {
 #pragma unroll
-          for (int db = 0; db < DB; ++db)
-            va[(ks + 1) & 1][db] = vcol(Vc, 16 * (ks + 1), 32 * db);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int db = 0; db < DB; ++db) mfma16(va[ks & 1][db], pv[ks], acc[db]);
-#pragma unroll
-        for (int j = 4 * ks; j < 4 * ks + 4; ++j) {
-          mx0 = fmaxf(mx0, sn[0][j]);
-          mx1 = fmaxf(mx1, sn[1][j]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
+        for (int db = 0; db < DB; ++db)
+          va[(ks + 1) & 1][db] = vcol(Vc, 16 * (ks + 1), 32 * db);
       }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) mfma16(va[ks & 1][db], pv[ks], acc[db]);
+#pragma unroll
+      for (int j = 4 * ks; j < 4 * ks + 4; ++j) {
+        mx0 = fmaxf(mx0, sn[0][j]);
+        mx1 = fmaxf(mx1, sn[1][j]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
     const float mx = swap32_max(fmaxf(mx0, mx1)) * c2;
     if (i1.valid) rescale(mx);
+  };
+  auto advance = [&]() {
     it = i1;
     i1 = i2;
     if (i2.valid) i2.next(geo, BN);
+  };
+  auto sync = [&]() {
     wait_all();
     __syncthreads();
+  };
+
+  // Two workgroups share a CU, one wave of each on every SIMD. At equal
+  // priority the SIMD issues for the older wave first, which then runs far
+  // ahead of its partner and leaves lone-wave tails at the end of the grid;
+  // alternating the issue priority every key tile shares the MFMA pipe.
+  // Each step first starts the copies of K(j+2) and V(j+1) into the stages
+  // step j-1 finished with (spreading them between the phase A MFMAs
+  // measured ~8% slower).
+  int hi_prio = 0;
+  auto step = [&](f32x16 (&sc)[2], f32x16 (&sn)[2], const char* Kn, const char* Vc, char* Kw,
+                  char* Vw) {
+    copy_k(i2, Kw);
+    copy_v(i1, Vw);
+    if (hi_prio) __builtin_amdgcn_s_setprio(1);
+    else __builtin_amdgcn_s_setprio(0);
+    hi_prio ^= 1;
+    phase_a(sc, sn, Kn);
+    phase_b(sn, Vc);
+    advance();
+    sync();
   };
   while (it.valid) {
     step(sa, sb, kb1, vb0, kb0, vb1);
@@ -307,7 +303,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const Args a) {
 
   // ---- epilogue: stage O^T (unnormalised), m, l through LDS ----------------
   float* Ow = reinterpret_cast<float*>(smem) + w * 32 * C::OSTR;
-  float* Ms = reinterpret_cast<float*>(smem) + 4 * 32 * C::OSTR;
+  float* Ms = reinterpret_cast<float*>(smem) + NW * 32 * C::OSTR;
   float* Ls = Ms + BM;
 #pragma unroll
   for (int db = 0; db < DB; ++db)
@@ -406,11 +402,12 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const Args a) {
 
 template <typename T, int D>
 static hipError_t launch_fwd_t(const Args& a, hipStream_t st) {
+  using C = FwdCfg<T, D>;
   const Geo geo{a.layout, a.cp, a.rank, a.T, a.Tkv};
-  const long long nt = (long long)geo.ntiles(FwdCfg<T, D>::BM) * a.B * a.H;
+  const long long nt = (long long)geo.ntiles(C::BM) * a.B * a.H;
   if (nt == 0) return hipSuccess;
   timing_mark(st);
-  hipLaunchKernelGGL((fwd_kernel<T, D>), dim3((unsigned)nt), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((fwd_kernel<T, D>), dim3((unsigned)nt), dim3(C::NT), 0, st, a);
   timing_mark(st);
   return hipGetLastError();
 }
@@ -420,7 +417,7 @@ hipError_t launch_fwd(const Args& a, int dtype, int D, hipStream_t st) {
   return D == 128 ? launch_fwd_t<float, 128>(a, st) : launch_fwd_t<float, 64>(a, st);
 }
 
-int fwd_tile_rows() { return 128; }
+int fwd_tile_rows() { return FwdCfg<bf16, 128>::BM; }
 int fwd_tile_keys() { return 64; }
 
 }  // namespace e3

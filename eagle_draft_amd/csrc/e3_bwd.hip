@@ -30,6 +30,7 @@
 //                 diagonals).
 #include "e3_common.h"
 
+
 namespace e3 {
 
 // ---------------------------------------------------------------------------
@@ -50,7 +51,8 @@ struct DkdvCfg {
   static constexpr int STAGE = 2 * RT;                  // Q, dO
   static constexpr int LSTAGE = 2 * BMQ * 4;            // lse2, delta
   static constexpr int PW = 64 * 16 * MB * (int)sizeof(T);   // P of one wave (per lane: 16 MB values)
-  static constexpr int LDS = 2 * STAGE + 2 * LSTAGE + 4 * PW;
+  static constexpr int NS = 3;                          // Q / dO stages
+  static constexpr int LDS = NS * STAGE + NS * LSTAGE + 2 * 4 * PW;   // + two P buffers
 };
 
 // Query tiles (rows of the share) that can see keys [k_lo, k_hi) with document
@@ -106,10 +108,10 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(const Args a) {
   constexpr int BNK = C::BNK, BMQ = C::BMQ, MB = C::MB, KS = C::KS, DB = C::DB, NW = C::NW;
   constexpr int sz = (int)sizeof(T);
   __shared__ __attribute__((aligned(16))) char smem[C::LDS];
-  // Stage p: Q at 0, dO at RT. Then the two lse2 / delta stages and the P
-  // exchange buffers.
-  char* const lb0 = smem + 2 * C::STAGE;
-  char* const pbuf = lb0 + 2 * C::LSTAGE;
+  // Stage p: Q at 0, dO at RT. Then the three lse2 / delta stages and the two
+  // sets of P exchange buffers.
+  char* const lb0 = smem + C::NS * C::STAGE;
+  char* const pbuf = lb0 + C::NS * C::LSTAGE;
   const unsigned sbase = lds_addr(smem);
 
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
@@ -189,22 +191,29 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(const Args a) {
       }
   };
 
-  QIter it, i1;
+  // Three stages and one barrier per step: the barrier of step j publishes P(j)
+  // and the copy of tile j+1, and by then every wave has finished step j-1, so
+  // tile j+2 is copied into the stage of tile j-1 right after it. Without an
+  // end-of-step barrier the P wave runs on into S(j+1) and its exponentials
+  // while the dS wave forms dS(j) and dK(j). P alternates between two buffers.
+  QIter it, i1, i2;
   it.begin(geo, kt0, q_hi, BMQ);
   i1 = it;
   if (i1.valid) i1.next(geo, BMQ);
+  i2 = i1;
+  if (i2.valid) i2.next(geo, BMQ);
   if (it.valid) dma_stage(0, it);
+  if (i1.valid) dma_stage(1, i1);
   wait_all();
   __syncthreads();
 
-  char* const pw = pbuf + kw * C::PW;   // P of this key block, lane-major
   const ColRead<T, C::RRB> rcol(lane);
+  int cur = 0;                          // stage of tile j (j mod 3)
   for (int par = 0; it.valid; par ^= 1) {
-    const int cur = __builtin_amdgcn_readfirstlane(par);
     const char* const st = smem + cur * C::STAGE;
     const float* const L2s = reinterpret_cast<const float*>(lb0 + cur * C::LSTAGE);
     const float* const Ds = L2s + BMQ;
-    if (i1.valid) dma_stage(cur ^ 1, i1);
+    char* const pw = pbuf + (par * 4 + kw) * C::PW;   // P(j) of this key block, lane-major
     // S^T (P waves, rows Q) or dP^T (dS waves, rows dO): lane = key.
     f32x16 sp[MB];
     {
@@ -235,7 +244,9 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(const Args a) {
         *reinterpret_cast<Op*>(pw + (q * 64 + lane) * (int)sizeof(Op)) = ops[q];
       }
     }
-    __syncthreads();   // P of the tile is in LDS
+    wait_all();
+    __syncthreads();   // P(j) and tile j+1 are in LDS; tile j-1's stage is free
+    if (i2.valid) dma_stage(cur == 0 ? 2 : cur - 1, i2);
     if (role == 1) {
 #pragma unroll
       for (int q = 0; q < BMQ / 16; ++q) {
@@ -261,9 +272,9 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(const Args a) {
         for (int db = 0; db < DB; ++db) mfma16(rcol(Cc, 16 * ks, 32 * db), ops[ks], acc[db]);
     }
     it = i1;
-    if (i1.valid) i1.next(geo, BMQ);
-    wait_all();
-    __syncthreads();   // the next stage is in LDS; this stage and P are free
+    i1 = i2;
+    if (i2.valid) i2.next(geo, BMQ);
+    cur = cur == 2 ? 0 : cur + 1;
   }
 
   // dV0 (P waves) or dK0 = scale * dK (dS waves); keys no query sees get zeros.

@@ -187,8 +187,8 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU's share on one GPU only; --gpus {args.gpus} "
-              f"(WORLD_SIZE={world}) is not supported: the multi-GPU path is not built "
-              "(collectives are out of scope for this build).", file=sys.stderr)
+              f"(WORLD_SIZE={world}) is not supported: the library runs one GPU's share "
+              "(full sequence, Ulysses head shard or zig-zag rank) and has no collectives.", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -11,7 +11,7 @@ from tests.parity import assert_within, compare, run_hip, run_oracle, say
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 12
+N_CASES = 24
 
 
 def _docs(rng, total):
@@ -28,8 +28,8 @@ def fuzz_case(i):
     rng = random.Random(1000 + i)
     dtype = "f32" if i % 4 == 3 else "bf16"
     D = rng.choice([64, 128])
-    H = rng.randint(1, 3)
-    nb = rng.randint(1, 5)
+    H = rng.randint(1, 3) if i < 12 else rng.randint(1, 6)
+    nb = rng.randint(1, 5) if i < 12 else rng.randint(1, 9)
     layout = ["full", "full", "headshard", "contiguous", "zigzag"][i % 5]
     kw = dict(dtype=dtype, D=D, H=H, num_blocks=nb, seed=i, layout=layout)
     if layout == "zigzag":

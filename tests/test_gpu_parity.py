@@ -1,7 +1,7 @@
 """GPU parity at sizes the oracle finishes in seconds: the HIP path (through the
 C ABI) against the CPU oracle, element by element, on the same seeded inputs.
-Cases span several tiles, ragged tails, several documents (one empty), one-row
-documents, num_blocks = 1, B > 1, both head dims and every layout."""
+Cases span several tiles, ragged tails, single-row sequences, several documents
+(one empty), one-row documents, num_blocks = 1, B > 1, both head dims and every layout."""
 import numpy as np
 import pytest
 import torch
@@ -36,6 +36,9 @@ CASES = {
     "zigzag_d64": W(S=512, H=2, D=64, num_blocks=3, layout="zigzag", cp=2, rank=0),
     "headshard": W(S=1536, H=2, D=128, num_blocks=4, layout="headshard", cp=4,
                    doc_lens=[512, 512, 256, 256]),
+    "bf16_single_row": W(S=1, H=2, D=128, num_blocks=3),
+    "f32_two_rows_d64": W(dtype="f32", S=2, H=1, D=64, num_blocks=2),
+    "zigzag_one_row_chunks": W(S=8, H=1, D=128, num_blocks=2, layout="zigzag", cp=4, rank=2),
 }
 
 

@@ -31,9 +31,13 @@ if ROOT not in sys.path:
 METRIC = "EAGLE-3 mixed attn fwd+bwd TFLOP/s (causal) + % bf16 MFMA peak, T=4096 H=32 D=128"
 PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}   # MI355X dense MFMA (bf16) / fp32 vector
 PEAK_GBS = 8000.0                               # MI355X HBM3E
-KERNELS = ["fwd", "dq", "dkdv", "diag_tail"]
-FWD_STAGES = ["fwd"]
-BWD_STAGES = ["dq", "dkdv", "diag_tail"]
+KERNELS = ["fwd", "dq", "dkdv", "diag_bwd", "diag_tail"]
+# Events the library records per call (see eagle3_set_timing_events): forward
+# e0 | fwd | e1; backward e0 | dq | e1, side stream e2 | diag_bwd | e3, main e1 |
+# dkdv | e4 | wait for the side stream | e5.
+NFWD_EV, NBWD_EV = 2, 6
+STAGE_EVENTS = {"fwd": ("f", 0, 1), "dq": ("b", 0, 1), "diag_bwd": ("b", 2, 3),
+                "dkdv": ("b", 1, 4), "diag_tail": ("b", 4, 5)}
 
 
 def log(msg):
@@ -95,9 +99,13 @@ def kernel_work(w, P0):
         # q, dO, O, k0, v0, lse read; delta, lse*log2(e) and dq (or its float32
         # partial) written; S, dP, dQ = 3 GEMMs
         "dq": dict(flop=6 * pf, diag_flop=0, bytes=3 * u + (2 if N else 1) * u + 2 * ukv + 3 * rowf),
-        # wait for the diagonal gradients: q, dO, kd, vd, dq partial read;
-        # dq, dkd, dvd written (the part of that kernel not hidden under dK/dV)
-        "diag_tail": dict(flop=0, diag_flop=10 * diagf, bytes=2 * u + 4 * N * u + 3 * u),
+        # closed-form diagonal gradients (side stream, beside dK/dV): q, dO, kd, vd,
+        # the float32 dq partial, lse*log2(e) and delta read; dq, dkd, dvd written
+        "diag_bwd": dict(flop=0, diag_flop=10 * diagf,
+                         bytes=(2 * u + 2 * N * u + 2 * u + 2 * rowf + u + 2 * N * u) if N else 0),
+        # the wait for the diagonal gradients after dK/dV: time only (the bytes are
+        # the diag_bwd kernel's, which mostly ran beside dK/dV)
+        "diag_tail": dict(flop=0, diag_flop=0, bytes=0),
     }
 
 
@@ -250,7 +258,7 @@ def main():
     log(f"[bench] {args.steps} steps: {total_ms:.3f} ms ({ms_per_step:.4f} ms/step, wall {wall_ms:.1f} ms)")
 
     # (2) per-kernel times: events recorded by the library around each kernel
-    nfwd, nbwd = len(FWD_STAGES) + 1, len(BWD_STAGES) + 1
+    nfwd, nbwd = NFWD_EV, NBWD_EV
     per = {k: [] for k in KERNELS}
     fwd_ms, bwd_ms, flushed = [], [], []
     flush_buf = None if args.no_flush else torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -273,10 +281,9 @@ def main():
     for r in range(reps):
         f0 = r * nfwd
         b0 = r * nbwd
-        for i, k in enumerate(FWD_STAGES):
-            per[k].append(ev.elapsed_ms(evf[f0 + i], evf[f0 + i + 1]))
-        for i, k in enumerate(BWD_STAGES):
-            per[k].append(ev.elapsed_ms(evb[b0 + i], evb[b0 + i + 1]))
+        for k, (which, i, j) in STAGE_EVENTS.items():
+            arr, base = (evf, f0) if which == "f" else (evb, b0)
+            per[k].append(ev.elapsed_ms(arr[base + i], arr[base + j]))
         fwd_ms.append(ev.elapsed_ms(evf[f0], evf[f0 + nfwd - 1]))
         bwd_ms.append(ev.elapsed_ms(evb[b0], evb[b0 + nbwd - 1]))
         flushed.append(fwd_ms[-1] + bwd_ms[-1])
@@ -292,11 +299,14 @@ def main():
         kw = work[k]
         kern[k] = {
             "us_mean": round(t_us, 2), "us_median": round(statistics.median(per[k]) * 1e3, 2),
-            "tflops": round(kw["flop"] / (t_us * 1e-6) / 1e12, 2) if kw["flop"] else 0.0,
-            "gbs": round(kw["bytes"] / (t_us * 1e-6) / 1e9, 1),
+            "tflops": round(kw["flop"] / (t_us * 1e-6) / 1e12, 2) if kw["flop"] and t_us > 0 else None,
+            "gbs": round(kw["bytes"] / (t_us * 1e-6) / 1e9, 1) if kw["bytes"] and t_us > 0 else None,
             "flop": kw["flop"], "bytes": kw["bytes"],
         }
-    dom = max(KERNELS, key=lambda k: kern[k]["us_mean"])
+    kern["diag_bwd"]["stream"] = "side (overlaps dkdv)"
+    kern["diag_tail"]["note"] = "time only: the wait for diag_bwd after dkdv"
+    # the dominant kernel: the longest of the kernels on the critical path
+    dom = max(("fwd", "dq", "dkdv", "diag_bwd"), key=lambda k: kern[k]["us_mean"])
     dk = kern[dom]
     t_dom = dk["us_mean"] * 1e-6
     peak_t = PEAK_TFLOPS[w.dtype]

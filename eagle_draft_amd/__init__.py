@@ -164,6 +164,16 @@ class Problem:
         s.kd_batch_stride = kd_batch_stride
         s.kd_block_stride = kd_block_stride
         self._s = s
+        # Element strides of the k/v tensors (block 0 and the diagonal blocks) and
+        # of their gradients; 0 in the arguments means dense.
+        HD = H * D
+        k0_bs = k0_batch_stride or T_kv * HD
+        kd_blk = kd_block_stride or T * HD
+        kd_bs = kd_batch_stride or (num_blocks - 1) * T * HD
+        self.k0_strides = (k0_bs, HD, D, 1)
+        self.kd_strides = (kd_bs, kd_blk, HD, D, 1)
+        self.dense_kv = (k0_bs == T_kv * HD and kd_blk == T * HD
+                         and kd_bs == (num_blocks - 1) * T * HD)
 
     def ref(self):
         return ctypes.byref(self._s)
@@ -206,7 +216,11 @@ class Problem:
         return int(n)
 
 
-def _check_tensor(name, t, shape, dtype, device):
+def _check_tensor(name, t, shape, dtype, device, strides=None):
+    """Checks device, dtype and shape, and that the memory layout is the dense
+    row-major one, or, for the k/v tensors, the one given by `strides` (in
+    elements; dimensions of size 1 are not checked). The inner [rows, H, D]
+    part must be dense either way."""
     if t is None:
         raise ValueError(f"{name} is required")
     if t.device != device:
@@ -215,8 +229,22 @@ def _check_tensor(name, t, shape, dtype, device):
         raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
     if tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
+    if strides is None:
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        return
+    for dim, (n, want, got) in enumerate(zip(t.shape, strides, t.stride())):
+        if n > 1 and want != got:
+            raise ValueError(f"{name} has strides {tuple(t.stride())}, expected {tuple(strides)} "
+                             f"(dimension {dim}); pass the strides in the Problem")
+
+
+def _strided_empty(shape, strides, dtype, device):
+    """An uninitialised tensor of the given shape and element strides."""
+    extent = 1 + sum((n - 1) * s for n, s in zip(shape, strides) if n > 0)
+    if any(n == 0 for n in shape):
+        extent = 0
+    return torch.empty(max(extent, 1), dtype=dtype, device=device).as_strided(shape, strides)
 
 
 def _entry(prob: Problem, kind: str):
@@ -229,11 +257,11 @@ def fwd(prob: Problem, q, k0, v0, kd=None, vd=None, out=None, lse=None):
     dev = q.device
     B, T, Tkv, H, D, N = prob.B, prob.T, prob.T_kv, prob.H, prob.D, prob.N
     _check_tensor("q", q, (B, T, H, D), prob.dtype, dev)
-    _check_tensor("k0", k0, (B, Tkv, H, D), prob.dtype, dev)
-    _check_tensor("v0", v0, (B, Tkv, H, D), prob.dtype, dev)
+    _check_tensor("k0", k0, (B, Tkv, H, D), prob.dtype, dev, prob.k0_strides)
+    _check_tensor("v0", v0, (B, Tkv, H, D), prob.dtype, dev, prob.k0_strides)
     if N > 0:
-        _check_tensor("kd", kd, (B, N, T, H, D), prob.dtype, dev)
-        _check_tensor("vd", vd, (B, N, T, H, D), prob.dtype, dev)
+        _check_tensor("kd", kd, (B, N, T, H, D), prob.dtype, dev, prob.kd_strides)
+        _check_tensor("vd", vd, (B, N, T, H, D), prob.dtype, dev, prob.kd_strides)
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
@@ -251,18 +279,28 @@ def bwd(prob: Problem, dout, q, k0, v0, kd, vd, out, lse, grads=None, workspace=
     dev = q.device
     B, T, Tkv, H, D, N = prob.B, prob.T, prob.T_kv, prob.H, prob.D, prob.N
     for name, t, shp in (("dout", dout, (B, T, H, D)), ("q", q, (B, T, H, D)),
-                         ("k0", k0, (B, Tkv, H, D)), ("v0", v0, (B, Tkv, H, D)),
                          ("out", out, (B, T, H, D))):
         _check_tensor(name, t, shp, prob.dtype, dev)
+    _check_tensor("k0", k0, (B, Tkv, H, D), prob.dtype, dev, prob.k0_strides)
+    _check_tensor("v0", v0, (B, Tkv, H, D), prob.dtype, dev, prob.k0_strides)
     _check_tensor("lse", lse, (B, H, T), torch.float32, dev)
     if N > 0:
-        _check_tensor("kd", kd, (B, N, T, H, D), prob.dtype, dev)
-        _check_tensor("vd", vd, (B, N, T, H, D), prob.dtype, dev)
+        _check_tensor("kd", kd, (B, N, T, H, D), prob.dtype, dev, prob.kd_strides)
+        _check_tensor("vd", vd, (B, N, T, H, D), prob.dtype, dev, prob.kd_strides)
     if grads is None:
-        grads = (torch.empty_like(q), torch.empty_like(k0), torch.empty_like(v0),
-                 torch.empty(B, N, T, H, D, dtype=prob.dtype, device=dev),
-                 torch.empty(B, N, T, H, D, dtype=prob.dtype, device=dev))
+        # gradients take the strides of the tensors they differentiate
+        grads = (torch.empty_like(q),
+                 _strided_empty((B, Tkv, H, D), prob.k0_strides, prob.dtype, dev),
+                 _strided_empty((B, Tkv, H, D), prob.k0_strides, prob.dtype, dev),
+                 _strided_empty((B, N, T, H, D), prob.kd_strides, prob.dtype, dev),
+                 _strided_empty((B, N, T, H, D), prob.kd_strides, prob.dtype, dev))
     dq, dk0, dv0, dkd, dvd = grads
+    _check_tensor("dq", dq, (B, T, H, D), prob.dtype, dev)
+    _check_tensor("dk0", dk0, (B, Tkv, H, D), prob.dtype, dev, prob.k0_strides)
+    _check_tensor("dv0", dv0, (B, Tkv, H, D), prob.dtype, dev, prob.k0_strides)
+    if N > 0:
+        _check_tensor("dkd", dkd, (B, N, T, H, D), prob.dtype, dev, prob.kd_strides)
+        _check_tensor("dvd", dvd, (B, N, T, H, D), prob.dtype, dev, prob.kd_strides)
     if workspace is None:
         workspace = torch.empty(max(prob.workspace_bytes(), 256), dtype=torch.uint8, device=dev)
     _check(_entry(prob, "bwd")(prob.ref(), _ptr(dout), _ptr(q), _ptr(k0), _ptr(v0),
@@ -290,6 +328,8 @@ def lse_merge(out, lse, block_out, block_lse, block_lse_layout: int = 0):
 
 
 class _CachedAttention(torch.autograd.Function):
+    """List form: separate q, k0, v0, kd, vd tensors."""
+
     @staticmethod
     def forward(ctx, prob, q, k0, v0, kd, vd):
         out, lse = fwd(prob, q, k0, v0, kd, vd)
@@ -304,15 +344,73 @@ class _CachedAttention(torch.autograd.Function):
         return None, dq, dk0, dv0, dkd, dvd
 
 
-def cached_attention(q: torch.Tensor, cache_k: Sequence[torch.Tensor], cache_v: Sequence[torch.Tensor],
-                     scale: float, cu_seqlens=None, layout: str = "full", cp: int = 1, rank: int = 0,
+class _CachedAttentionStacked(torch.autograd.Function):
+    """Stacked form: cache_k / cache_v [B, nb, T, H, D] (dense). Block 0 and the
+    diagonal blocks are views of the cache passed to the kernels through their
+    batch and block strides; the gradients of the caches are written the same way
+    into one [B, nb, T, H, D] buffer each. With a separate block-0 k0/v0 (a ring
+    share), the cache's block 0 is unused and gets a zero gradient."""
+
+    @staticmethod
+    def forward(ctx, prob, q, cache_k, cache_v, k0, v0):
+        own = k0 is None
+        kk0 = cache_k[:, 0] if own else k0
+        vv0 = cache_v[:, 0] if own else v0
+        out, lse = fwd(prob, q, kk0, vv0, cache_k[:, 1:], cache_v[:, 1:])
+        ctx.prob, ctx.own = prob, own
+        ctx.save_for_backward(q, cache_k, cache_v, kk0, vv0, out, lse)
+        return out
+
+    @staticmethod
+    def backward(ctx, dout):
+        q, cache_k, cache_v, k0, v0, out, lse = ctx.saved_tensors
+        prob = ctx.prob
+        dck = torch.empty_like(cache_k)
+        dcv = torch.empty_like(cache_v)
+        if ctx.own:
+            dk0, dv0 = dck[:, 0], dcv[:, 0]
+        else:
+            dck[:, 0].zero_()
+            dcv[:, 0].zero_()
+            dk0, dv0 = torch.empty_like(k0), torch.empty_like(v0)
+        grads = (torch.empty_like(q), dk0, dv0, dck[:, 1:], dcv[:, 1:])
+        dq, dk0, dv0, _, _ = bwd(prob, dout.contiguous(), q, k0, v0, cache_k[:, 1:], cache_v[:, 1:],
+                                 out, lse, grads=grads)
+        if ctx.own:
+            return None, dq, dck, dcv, None, None
+        return None, dq, dck, dcv, dk0, dv0
+
+
+def cached_attention(q: torch.Tensor, cache_k, cache_v, scale: float, cu_seqlens=None,
+                     layout: str = "full", cp: int = 1, rank: int = 0,
                      k0: Optional[torch.Tensor] = None, v0: Optional[torch.Tensor] = None):
-    """EAGLE-3 mixed attention with autograd, in the list form of the pages'
-    cached_*_attention: cache_k / cache_v are lists of [B, T, H, D] (index 0 = the
-    step-0 sequence, 1.. = TTT steps). For a ring share (contiguous / zig-zag),
-    pass the full-sequence block-0 k0/v0 [B, T_kv, H, D] explicitly; cache_k[0] is
-    then ignored. Returns out [B, T, H, D] in q's dtype."""
+    """EAGLE-3 mixed attention with autograd, in the forms of the pages'
+    cached_*_attention (ring_attention page, `cached_ring_attention`;
+    `_CachedRingAttention` stacks the lists into [B, nb, T, H, D]):
+      - cache_k / cache_v as lists of [B, T, H, D] (index 0 = the step-0 sequence,
+        1.. = TTT steps); the TTT blocks are stacked (one copy);
+      - cache_k / cache_v as dense [B, nb, T, H, D] tensors: no copy, the blocks
+        are read and their gradients written through strides.
+    For a ring share (contiguous / zig-zag), pass the full-sequence block-0 k0/v0
+    [B, T_kv, H, D] explicitly; the cache's block 0 is then ignored. Returns out
+    [B, T, H, D] in q's dtype."""
     B, T, H, D = q.shape
+    if isinstance(cache_k, torch.Tensor):
+        if not (isinstance(cache_v, torch.Tensor) and cache_k.shape == cache_v.shape
+                and cache_k.dim() == 5 and cache_k.is_contiguous() and cache_v.is_contiguous()):
+            raise ValueError("stacked caches must be dense [B, nb, T, H, D] tensors of one shape")
+        nb = cache_k.shape[1]
+        if tuple(cache_k.shape) != (B, nb, T, H, D):
+            raise ValueError(f"cache shape {tuple(cache_k.shape)} does not match q {tuple(q.shape)}")
+        Tkv = T if k0 is None else k0.shape[1]
+        blk = nb * T * H * D
+        prob = Problem(B, T, Tkv, H, D, nb, scale, dtype=q.dtype, layout=layout, cp=cp,
+                       rank=rank, cu_seqlens=cu_seqlens, device=q.device,
+                       k0_batch_stride=blk if k0 is None else 0, kd_batch_stride=blk,
+                       kd_block_stride=T * H * D)
+        return _CachedAttentionStacked.apply(
+            prob, q.contiguous(), cache_k, cache_v,
+            None if k0 is None else k0.contiguous(), None if v0 is None else v0.contiguous())
     k0 = cache_k[0] if k0 is None else k0
     v0 = cache_v[0] if v0 is None else v0
     nb = len(cache_k)

@@ -107,8 +107,13 @@ int validate(const e3_problem* p, Resolved& r, bool whole, bool need_dev = true)
       return fail(E3_EINVAL, "cu_seqlens ends at %d, the sequence length is %lld", cu[p->num_docs], Tkv);
     if (p->num_docs > 1) {
       if (p->B != 1) return fail(E3_EINVAL, "several documents (varlen) need B == 1");
-      if (p->layout == E3_LAYOUT_ZIGZAG)
-        return fail(E3_EUNSUPPORTED, "several documents with the ZIGZAG layout (per-document halving) are not supported");
+      if (p->layout == E3_LAYOUT_ZIGZAG) {
+        // every document is cut into 2cp chunks (zigzag_ring_attention page, `get_half_index`)
+        for (int i = 0; i < p->num_docs; ++i)
+          if ((cu[i + 1] - cu[i]) % (2 * p->cp) != 0)
+            return fail(E3_EINVAL, "ZIGZAG: document %d has length %d, not a multiple of 2*cp = %d", i,
+                        cu[i + 1] - cu[i], 2 * p->cp);
+      }
       if (need_dev && !p->cu_seqlens_dev)
         return fail(E3_EINVAL, "cu_seqlens_dev is NULL with num_docs=%d", p->num_docs);
     }
@@ -120,14 +125,27 @@ int validate(const e3_problem* p, Resolved& r, bool whole, bool need_dev = true)
   r.kd_bs = p->kd_batch_stride ? p->kd_batch_stride : (long long)r.N * T * HD;
   if (r.k0_bs < 0 || r.kd_blk < 0 || r.kd_bs < 0 || (r.k0_bs % 8) || (r.kd_blk % 8) || (r.kd_bs % 8))
     return fail(E3_EINVAL, "strides must be non-negative multiples of 8 elements");
+  // Rows of different batch rows or blocks must not overlap: the gradients are
+  // written through the same strides, and overlapping rows would race.
+  if (p->B > 1 && r.k0_bs < Tkv * HD)
+    return fail(E3_EINVAL, "k0_batch_stride %lld < T_kv*H*D = %lld (batch rows would overlap)", r.k0_bs, Tkv * HD);
+  if (r.N > 1 && r.kd_blk < T * HD)
+    return fail(E3_EINVAL, "kd_block_stride %lld < T*H*D = %lld (blocks would overlap)", r.kd_blk, T * HD);
+  if (p->B > 1 && r.N > 0 && r.kd_bs < (long long)(r.N - 1) * r.kd_blk + T * HD)
+    return fail(E3_EINVAL, "kd_batch_stride %lld < (N-1)*kd_block_stride + T*H*D = %lld (batch rows would overlap)",
+                r.kd_bs, (long long)(r.N - 1) * r.kd_blk + T * HD);
   return E3_OK;
 }
 
-e3::Geo geo_of(const e3_problem* p) { return e3::Geo{p->layout, p->cp, p->rank, p->T, p->T_kv}; }
+e3::Geo geo_of(const e3_problem* p) {
+  return e3::Geo{p->layout, p->cp, p->rank, p->T, p->T_kv, p->num_docs > 1 ? p->cu_seqlens_host : nullptr,
+                 p->num_docs > 1 ? p->num_docs : 1};
+}
 
 e3::Args make_args(const e3_problem* p, const Resolved& r) {
   e3::Args a{};
   a.cu = p->num_docs > 1 ? p->cu_seqlens_dev : nullptr;
+  a.cu_host = p->num_docs > 1 ? p->cu_seqlens_host : nullptr;
   a.ndocs = p->num_docs > 1 ? p->num_docs : 1;
   a.B = p->B;
   a.T = p->T;
@@ -193,7 +211,7 @@ struct BwdWs {
 
 BwdWs bwd_ws_layout(const e3_problem* p) {
   BwdWs l;
-  l.pitch = geo_of(p).qruns().pitch;
+  l.pitch = geo_of(p).pitch();
   const size_t rows = (size_t)p->B * p->H * l.pitch;       // multiple of 64
   l.delta = rows * sizeof(float);
   l.dqd = 2 * rows * sizeof(float);

@@ -126,7 +126,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(const Args a) {
   const int BH = a.B * a.H;
   const int kt = blockIdx.x / BH, bh = blockIdx.x % BH,
             b = bh / a.H, h = bh % a.H;
-  const Geo geo{a.layout, a.cp, a.rank, a.T, a.Tkv};
+  const Geo geo{a.layout, a.cp, a.rank, a.T, a.Tkv, a.cu, a.ndocs};
   const int kt0 = kt * BNK;
   const int kt1 = (kt0 + BNK) < a.Tkv ? (kt0 + BNK) : a.Tkv;
 
@@ -141,8 +141,10 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(const Args a) {
   const unsigned rrow = (unsigned)(rs * sz);
 
   // This lane's key; a query at global position gm sees it iff s <= gm < s_hi.
+  // In ring-step mode only the keys held at the launch's ring step count.
   const int s = kt0 + kw * 32 + l32;
-  const bool svalid = s < a.Tkv;
+  const bool svalid = s < a.Tkv && (!a.kv_accum || geo.in_step(s, a.step_lo));
+  if (a.kv_accum && !__syncthreads_or(svalid)) return;   // no key of the step in this tile
   const int s_hi = svalid ? doc_hi_of(a.cu, a.ndocs, s, a.Tkv) : 0;
   Op kv[KS];   // K (P waves) or V (dS waves) of this lane's key
 #pragma unroll
@@ -229,7 +231,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(const Args a) {
     }
     Op ops[BMQ / 16];
     if (role == 0) {
-      if (!interior(it)) mask(sp, it);
+      if (a.kv_accum || !interior(it)) mask(sp, it);   // ring-step mode: keys outside the step are masked
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -278,7 +280,21 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(const Args a) {
   }
 
   // dV0 (P waves) or dK0 = scale * dK (dS waves); keys no query sees get zeros.
-  if (svalid) {
+  // Ring-step mode adds into the float32 accumulators of the step's keys.
+  if (svalid && a.kv_accum) {
+    const float f = role ? a.scale : 1.f;
+    float* ob = reinterpret_cast<float*>(role ? a.dk0 : a.dv0) + (long long)b * a.k0_bs + (long long)h * D +
+                (long long)s * rs;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        f32x4 x = *reinterpret_cast<const f32x4*>(ob + 32 * db + 8 * jj + 4 * g);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] += acc[db][4 * jj + i] * f;
+        *reinterpret_cast<f32x4*>(ob + 32 * db + 8 * jj + 4 * g) = x;
+      }
+  } else if (svalid) {
     const float f = role ? a.scale : 1.f;
     T* ob = reinterpret_cast<T*>(role ? a.dk0 : a.dv0) + (long long)b * a.k0_bs + (long long)h * D +
             (long long)s * rs;
@@ -329,7 +345,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void dq_kernel(const A
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int BH = a.B * a.H;
   const int trank = blockIdx.x / BH, bh = blockIdx.x % BH, b = bh / a.H, h = bh % a.H;
-  const Geo geo{a.layout, a.cp, a.rank, a.T, a.Tkv};
+  const Geo geo{a.layout, a.cp, a.rank, a.T, a.Tkv, a.cu, a.ndocs};
   int row0, nrows, gpos0;
   geo.qtile(trank, BM, row0, nrows, gpos0);
 
@@ -409,7 +425,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void dq_kernel(const A
   };
 
   SegIter it, i1;
-  it.begin(geo, lo_min, g_max + 1, BN);
+  it.begin(geo, lo_min, g_max + 1, BN, a.step_lo, a.step_hi);
   i1 = it;
   if (i1.valid) i1.next(geo, BN);
   if (it.valid) dma_stage(0, it.s0);
@@ -496,8 +512,17 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void dq_kernel(const A
     f32x8 dqv = *reinterpret_cast<const f32x8*>(Qw + rr * C::OSTR + cc);
 #pragma unroll
     for (int e = 0; e < 8; ++e) dqv[e] *= a.scale;
-    if (a.N > 0) *reinterpret_cast<f32x8*>(dqdb + row * rs) = dqv;
-    else store8f(dqb + row * rs, dqv);
+    if (a.dq_accum) {
+      // ring-step mode: this launch's ring steps add into the caller's float32 dq
+      f32x8 acc = *reinterpret_cast<const f32x8*>(dqdb + row * rs);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += dqv[e];
+      *reinterpret_cast<f32x8*>(dqdb + row * rs) = acc;
+    } else if (a.N > 0) {
+      *reinterpret_cast<f32x8*>(dqdb + row * rs) = dqv;
+    } else {
+      store8f(dqb + row * rs, dqv);
+    }
   }
 }
 
@@ -516,7 +541,7 @@ __global__ __launch_bounds__(256, 4) void diag_bwd_kernel(const Args a) {
   constexpr int GPB = 256 / LPR;           // row groups per workgroup
   constexpr int NB = sizeof(T) == 2 ? 4 : 2;   // blocks per load group (fits 128 VGPRs)
   using V = typename V8<T>::type;
-  const Geo geo{a.layout, a.cp, a.rank, a.T, a.Tkv};
+  const Geo geo{a.layout, a.cp, a.rank, a.T, a.Tkv, a.cu, a.ndocs};
   const int tid = threadIdx.x, cc = (tid % LPR) * 8;
   const long long nrow = (long long)a.B * a.T * a.H;
   const long long rs = (long long)a.H * D;
@@ -530,7 +555,16 @@ __global__ __launch_bounds__(256, 4) void diag_bwd_kernel(const Args a) {
     const long long loff = ((long long)b * a.H + h) * a.q_pitch + geo.prow(t);
     const V qv = load8(reinterpret_cast<const T*>(a.q) + qoff);
     const V ov = load8(reinterpret_cast<const T*>(a.dout) + qoff);
-    const float l2 = a.lse2[loff], dl = a.delta[loff];
+    float l2, dl;
+    if (a.diag_self) {
+      // ring-step mode: delta = <dO, O> and lse*log2(e) formed here from the merged out/lse
+      const V oo = load8(reinterpret_cast<const T*>(a.o_in) + qoff);
+      dl = group_sum<LPR>(dot8(ov, oo, 0.f));
+      l2 = a.lse_in[((long long)b * a.H + h) * a.T + t] * kLog2e;
+    } else {
+      l2 = a.lse2[loff];
+      dl = a.delta[loff];
+    }
     f32x8 dq = *reinterpret_cast<const f32x8*>(a.dqd + qoff);   // scale * dQ(block 0)
     for (int i0 = 0; i0 < a.N; i0 += NB) {
       const int n = (a.N - i0) < NB ? (a.N - i0) : NB;
@@ -567,14 +601,13 @@ __global__ __launch_bounds__(256, 4) void diag_bwd_kernel(const Args a) {
   }
 }
 
-// Order (marks between the stages for the timing hook):
-//   main:  delta | K^T | dQ | (join Q^T, dO^T) dK/dV | (join diagonal)
-//   side:          Q^T, dO^T                 ... diagonal gradients (after dQ)
-// The Q^T / dO^T transposes overlap the dQ kernel and the diagonal gradients
-// (memory-bound) overlap the dK/dV kernel.
+// Order, with the timing hook's marks m0..m5:
+//   main:  m0 dQ (also writes delta and lse*log2(e)) m1 | dK/dV m4 | join m5
+//   side:                    (forked at m1) m2 diagonal gradients m3
+// The diagonal gradients (memory-bound) overlap the dK/dV kernel (MFMA-bound).
 template <typename T, int D>
 static hipError_t launch_bwd_t(const Args& a, hipStream_t st) {
-  const Geo geo{a.layout, a.cp, a.rank, a.T, a.Tkv};
+  const Geo geo{a.layout, a.cp, a.rank, a.T, a.Tkv, a.cu_host, a.ndocs};
   const long long nrow = (long long)a.B * a.H * a.q_pitch;
   if (nrow == 0) return hipSuccess;
   hipError_t e;
@@ -588,8 +621,13 @@ static hipError_t launch_bwd_t(const Args& a, hipStream_t st) {
   if (a.N > 0) {
     hipStream_t side = nullptr;
     if ((e = side_begin(st, 0, side)) != hipSuccess) return e;
+    timing_mark(side);
     hipLaunchKernelGGL((diag_bwd_kernel<T, D>), dim3(kDiagGrid), dim3(256), 0, side, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    timing_mark(side);
+  } else {
+    timing_mark(st);   // no diagonal blocks: the side-stream marks are empty stages
+    timing_mark(st);
   }
   const long long nk = (long long)((a.Tkv + DkdvCfg<T, D>::BNK - 1) / DkdvCfg<T, D>::BNK) * a.B * a.H;
   if (nk > 0) {
@@ -600,6 +638,20 @@ static hipError_t launch_bwd_t(const Args& a, hipStream_t st) {
   if (a.N > 0 && (e = side_end(st, 0)) != hipSuccess) return e;
   timing_mark(st);
   return hipSuccess;
+}
+
+// Ring-step mode: the closed-form diagonal gradients alone, on the caller's
+// stream, with delta and lse*log2(e) formed in the kernel (diag_self).
+template <typename T, int D>
+static hipError_t launch_diag_bwd_t(const Args& a, hipStream_t st) {
+  if ((long long)a.B * a.T * a.H == 0) return hipSuccess;
+  hipLaunchKernelGGL((diag_bwd_kernel<T, D>), dim3(kDiagGrid), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_diag_bwd(const Args& a, int dtype, int D, hipStream_t st) {
+  if (dtype == 0) return D == 128 ? launch_diag_bwd_t<bf16, 128>(a, st) : launch_diag_bwd_t<bf16, 64>(a, st);
+  return D == 128 ? launch_diag_bwd_t<float, 128>(a, st) : launch_diag_bwd_t<float, 64>(a, st);
 }
 
 hipError_t launch_bwd(const Args& a, int dtype, int D, hipStream_t st) {

@@ -44,22 +44,22 @@ struct Args {
   void* dvd;
   int q_pitch;          // positions per (b, h) row of lse2 / delta
   const int32_t* cu;    // device cu_seqlens (global document boundaries)
+  const int32_t* cu_host;   // host copy of the same (host-side geometry of a launch)
   int ndocs;            // <= 1: one document
   int B, T, Tkv, H, N;
   long long k0_bs, kd_bs, kd_blk;
   float scale;
   float c2;             // scale * log2(e): scores are kept in the base-2 domain
   int layout, cp, rank;
+  // Ring-step mode (the single-GPU half of the ring protocol): only the block-0
+  // keys of ring steps [step_lo, step_hi) are visited, and
+  int step_lo, step_hi;
+  int out_f32;          //   the forward writes a float32 (out, lse) of those keys
+  int dq_accum;         //   the dQ kernel adds scale * dQ into a float32 dq (dqd)
+  int kv_accum;         //   dK/dV adds into float32 dk0/dv0 for the steps' keys only
+  int diag_self;        //   the diagonal kernel forms delta and lse*log2(e) itself
 };
 
-// Row runs of the local queries: run i holds local rows [src[i], src[i]+len[i]) at
-// positions [dst[i], dst[i]+len[i]) of a padded per-(b, h) layout of `pitch`
-// positions, each run starting at a multiple of 64.
-struct XRuns {
-  int n;
-  int src[2], len[2], dst[2];
-  int pitch;
-};
 
 
 // Measurement hook (host): records the next caller-provided timing event, if any,
@@ -80,24 +80,66 @@ constexpr int kDiagGrid = 256;   // persistent grid of the diagonal-gradient ker
 // Share geometry (host and device)
 // ---------------------------------------------------------------------------
 
+// Document bounds from cu_seqlens (non-decreasing, cu[0] = 0, cu[nd] = S).
+__host__ __device__ inline int doc_lo_of(const int32_t* cu, int nd, int pos) {
+  if (nd <= 1) return 0;
+  int lo = 0, hi = nd;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (cu[mid] <= pos) lo = mid; else hi = mid;
+  }
+  return cu[lo];
+}
+__host__ __device__ inline int doc_hi_of(const int32_t* cu, int nd, int pos, int S) {
+  if (nd <= 1) return S;
+  int lo = 0, hi = nd;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (cu[mid] <= pos) lo = mid; else hi = mid;
+  }
+  return cu[hi];
+}
+
 // Query rows of a share come in runs of contiguous global positions:
 //   full / head shard: one run, positions 0..T-1
 //   contiguous rank r: one run, positions r*T .. r*T+T-1
-//   zig-zag rank r: run 0 = chunk r (early), run 1 = chunk 2cp-1-r (late), c = T/2 each
+//   zig-zag rank r: every document [dlo, dhi) (one document = the whole sequence)
+//     is cut into 2cp chunks of c = (dhi - dlo) / 2cp; the share holds, document by
+//     document, chunk r (early) then chunk 2cp-1-r (late) (zigzag_ring_attention
+//     page: module text, and `get_half_index`, which picks the front and back half
+//     of each varlen document), so document d's runs are 2d and 2d+1 and start at
+//     local row dlo / cp.
 // Block-0 K/V segments are visited in ring order: ring step j holds rank
-// (r - j) mod cp's K/V, i.e. chunk src (contiguous) or chunks {src, 2cp-1-src}
-// (zig-zag).
+// (r - j) mod cp's K/V, i.e. chunk src (contiguous) or, of the query's document,
+// chunks {src, 2cp-1-src} (zig-zag).
 struct Geo {
   int layout, cp, rank, T, Tkv;
+  const int32_t* cu;   // global document boundaries (host or device copy), or null
+  int nd;              // documents; <= 1: one document spanning the sequence
 
-  __host__ __device__ int nruns() const { return layout == LAYOUT_ZIGZAG ? 2 : 1; }
+  __host__ __device__ bool multidoc() const { return nd > 1 && cu != nullptr; }
+  __host__ __device__ int ndoc() const { return multidoc() ? nd : 1; }
+  __host__ __device__ void doc(int d, int& dlo, int& dhi) const {
+    if (multidoc()) {
+      dlo = cu[d];
+      dhi = cu[d + 1];
+    } else {
+      dlo = 0;
+      dhi = Tkv;
+    }
+  }
+
+  __host__ __device__ int nruns() const { return layout == LAYOUT_ZIGZAG ? 2 * ndoc() : 1; }
 
   __host__ __device__ void run(int i, int& lstart, int& len, int& gbase) const {
     if (layout == LAYOUT_ZIGZAG) {
-      const int c = T / 2;
-      lstart = i * c;
+      int dlo, dhi;
+      doc(i >> 1, dlo, dhi);
+      const int c = (dhi - dlo) / (2 * cp);
+      const int late = i & 1;
+      lstart = dlo / cp + late * c;
       len = c;
-      gbase = (i == 0 ? rank : 2 * cp - 1 - rank) * c;
+      gbase = dlo + (late ? 2 * cp - 1 - rank : rank) * c;
     } else {
       lstart = 0;
       len = T;
@@ -105,21 +147,60 @@ struct Geo {
     }
   }
 
+  // Run holding local row `row` (zig-zag: the row's document, then its half).
+  __host__ __device__ int run_of(int row) const {
+    if (layout != LAYOUT_ZIGZAG) return 0;
+    int d = 0;
+    if (multidoc()) {
+      int lo = 0, hi = nd;          // last document whose local start is <= row
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (cu[mid] / cp <= row) lo = mid; else hi = mid;
+      }
+      d = lo;
+    }
+    int dlo, dhi;
+    doc(d, dlo, dhi);
+    const int c = (dhi - dlo) / (2 * cp);
+    return 2 * d + (row - dlo / cp >= c ? 1 : 0);
+  }
+
   __host__ __device__ int nsteps() const {
     return (layout == LAYOUT_CONTIGUOUS || layout == LAYOUT_ZIGZAG) ? cp : 1;
   }
+
+  // Whether block-0 key s is held at ring step `step` (rank (rank - step) mod cp's
+  // K/V: its contiguous shard, or chunks {src, 2cp-1-src} of every document).
+  __host__ __device__ bool in_step(int s, int step) const {
+    if (layout == LAYOUT_CONTIGUOUS) {
+      const int src = ((rank - step) % cp + cp) % cp;
+      return s >= src * T && s < src * T + T;
+    }
+    if (layout == LAYOUT_ZIGZAG) {
+      const int src = ((rank - step) % cp + cp) % cp;
+      const int dlo = multidoc() ? doc_lo_of(cu, nd, s) : 0;
+      const int dhi = multidoc() ? doc_hi_of(cu, nd, s, Tkv) : Tkv;
+      const int c = (dhi - dlo) / (2 * cp);
+      if (c == 0) return false;
+      const int ch = (s - dlo) / c;
+      return ch == src || ch == 2 * cp - 1 - src;
+    }
+    return step == 0;
+  }
   __host__ __device__ int nparts() const { return layout == LAYOUT_ZIGZAG ? 2 : 1; }
 
-  __host__ __device__ void seg(int step, int part, int& a, int& b) const {
+  // Keys [a, b) of part `part` of ring step `step`; for the zig-zag layout, of the
+  // document [dlo, dlo + dlen) the query lies in.
+  __host__ __device__ void seg(int step, int part, int dlo, int dlen, int& a, int& b) const {
     if (layout == LAYOUT_CONTIGUOUS) {
       const int src = ((rank - step) % cp + cp) % cp;
       a = src * T;
       b = a + T;
     } else if (layout == LAYOUT_ZIGZAG) {
-      const int c = T / 2;
+      const int c = dlen / (2 * cp);
       const int src = ((rank - step) % cp + cp) % cp;
       const int id = part == 0 ? src : 2 * cp - 1 - src;
-      a = id * c;
+      a = dlo + id * c;
       b = a + c;
     } else {
       a = 0;
@@ -127,42 +208,29 @@ struct Geo {
     }
   }
 
-  // Position of local row `row` in the per-run, 64-aligned layout of qruns().
+  // Padded per-(b, h) row layout of lse*log2(e) and delta: run i occupies
+  // [P_i, P_i + roundup64(len_i)) with P_i = roundup4(lstart_i) + 68 i, so every
+  // 64-row query tile of a run starts on a 16-byte boundary and tiles never
+  // reach into the next run (P_{i+1} - P_i >= len_i + 65). One run: P_0 = 0.
+  __host__ __device__ int run_pad_start(int i) const {
+    int ls, len, gb;
+    run(i, ls, len, gb);
+    return (ls + 3) / 4 * 4 + 68 * i;
+  }
   __host__ __device__ int prow(int row) const {
-    if (layout == LAYOUT_ZIGZAG) {
-      const int c = T / 2;
-      return row < c ? row : (c + 63) / 64 * 64 + (row - c);
-    }
-    return row;
+    if (layout != LAYOUT_ZIGZAG) return row;
+    const int i = run_of(row);
+    int ls, len, gb;
+    run(i, ls, len, gb);
+    return run_pad_start(i) + (row - ls);
   }
-
-  // Inverse of prow: the local row at padded position p, or -1 for padding.
-  __host__ __device__ int trow(int p) const {
-    if (layout == LAYOUT_ZIGZAG) {
-      const int c = T / 2, c64 = (c + 63) / 64 * 64;
-      if (p < c) return p;
-      if (p < c64 || p - c64 >= c) return -1;
-      return c + (p - c64);
-    }
-    return p < T ? p : -1;
-  }
-
-  // Transposed-copy layout of the local query rows (one entry per run) and of
-  // the block-0 keys (one run).
-  __host__ __device__ XRuns qruns() const {
-    XRuns r{};
-    r.n = nruns();
-    int p = 0;
-    for (int i = 0; i < r.n; ++i) {
-      int ls, len, gb;
-      run(i, ls, len, gb);
-      r.src[i] = ls;
-      r.len[i] = len;
-      r.dst[i] = p;
-      p += (len + 63) / 64 * 64;
-    }
-    r.pitch = p;
-    return r;
+  // Positions per (b, h) of that layout (a multiple of 64).
+  __host__ __device__ int pitch() const {
+    const int n = nruns();
+    int ls, len, gb;
+    run(n - 1, ls, len, gb);
+    const int p = run_pad_start(n - 1) + (len + 63) / 64 * 64;
+    return (p + 63) / 64 * 64;
   }
 
   // Number of query tiles of height BM over all runs.
@@ -204,18 +272,19 @@ struct Geo {
 // segment in ring order, each segment clipped to the key window [wlo, whi).
 // Tile starts are multiples of BN (one tile grid per head, so the tiles are shared in L2); keys
 // of a tile outside [a, b) or outside a row's visible range are masked by the
-// kernel.
+// kernel. The window lies inside one document for the zig-zag layout (a query
+// tile lies inside one chunk of one document), whose chunks give the segments.
 struct SegIter {
-  int step, part, a, b, s0, end, wlo, whi;
+  int step, part, a, b, s0, end, wlo, whi, dlo, dlen, shi;
   bool valid;
 
   __host__ __device__ void seek(const Geo& g, int BN) {
     while (true) {
-      if (step >= g.nsteps()) {
+      if (step >= shi) {
         valid = false;
         return;
       }
-      g.seg(step, part, a, b);
+      g.seg(step, part, dlo, dlen, a, b);
       const int lo = a > wlo ? a : wlo;
       const int hi = b < whi ? b : whi;
       if (lo < hi) {
@@ -230,11 +299,20 @@ struct SegIter {
       }
     }
   }
-  __host__ __device__ void begin(const Geo& g, int wlo_, int whi_, int BN) {
+  // Ring steps [slo, shi) (clipped to the layout's steps).
+  __host__ __device__ void begin(const Geo& g, int wlo_, int whi_, int BN, int slo = 0,
+                                 int shi_ = 1 << 30) {
     wlo = wlo_;
     whi = whi_;
-    step = 0;
+    step = slo;
+    shi = shi_ < g.nsteps() ? shi_ : g.nsteps();
     part = 0;
+    dlo = 0;
+    dlen = g.Tkv;
+    if (g.layout == LAYOUT_ZIGZAG && g.multidoc()) {
+      dlo = doc_lo_of(g.cu, g.nd, wlo_);
+      dlen = doc_hi_of(g.cu, g.nd, wlo_, g.Tkv) - dlo;
+    }
     seek(g, BN);
   }
   __host__ __device__ void next(const Geo& g, int BN) {
@@ -247,26 +325,6 @@ struct SegIter {
     seek(g, BN);
   }
 };
-
-// Document bounds from cu_seqlens (non-decreasing, cu[0] = 0, cu[nd] = S).
-__host__ __device__ inline int doc_lo_of(const int32_t* cu, int nd, int pos) {
-  if (nd <= 1) return 0;
-  int lo = 0, hi = nd;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (cu[mid] <= pos) lo = mid; else hi = mid;
-  }
-  return cu[lo];
-}
-__host__ __device__ inline int doc_hi_of(const int32_t* cu, int nd, int pos, int S) {
-  if (nd <= 1) return S;
-  int lo = 0, hi = nd;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (cu[mid] <= pos) lo = mid; else hi = mid;
-  }
-  return cu[hi];
-}
 
 // ---------------------------------------------------------------------------
 // Device helpers

@@ -38,7 +38,9 @@ struct FwdCfg {
 
 constexpr float kRescaleSlack = 8.0f;      // log2 of the largest un-rescaled growth
 
-template <typename T, int D>
+// TO: element type of out (T; float for the float32 partials of ring-step mode,
+// where a row that sees no key of the visited steps gets out = 0, lse = -inf).
+template <typename T, int D, typename TO>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(const Args a) {
   using C = FwdCfg<T, D>;
   constexpr int NW = C::NW;
@@ -50,7 +52,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const Args a) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int BH = a.B * a.H;
   const int trank = blockIdx.x / BH, bh = blockIdx.x % BH, b = bh / a.H, h = bh % a.H;
-  const Geo geo{a.layout, a.cp, a.rank, a.T, a.Tkv};
+  const Geo geo{a.layout, a.cp, a.rank, a.T, a.Tkv, a.cu, a.ndocs};
   int row0, nrows, gpos0;
   geo.qtile(trank, BM, row0, nrows, gpos0);
 
@@ -166,7 +168,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const Args a) {
   // the MFMAs of O^T += V^T P^T for tile j with the mask and row max of tile
   // j+1. Tiles j, j+1, j+2 of the walk are it, i1, i2.
   SegIter it, i1, i2;
-  it.begin(geo, lo_min, g_max + 1, BN);
+  it.begin(geo, lo_min, g_max + 1, BN, a.step_lo, a.step_hi);
   i1 = it;
   if (i1.valid) i1.next(geo, BN);
   i2 = i1;
@@ -332,7 +334,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const Args a) {
   const int lr = lane / LPR, cc = (lane % LPR) * 8;
   const T* kdb = reinterpret_cast<const T*>(a.kd) + (long long)b * a.kd_bs + (long long)h * D + cc;
   const T* vdb = reinterpret_cast<const T*>(a.vd) + (long long)b * a.kd_bs + (long long)h * D + cc;
-  T* ob = reinterpret_cast<T*>(a.out) + (long long)b * a.T * rs + (long long)h * D + cc;
+  TO* ob = reinterpret_cast<TO*>(a.out) + (long long)b * a.T * rs + (long long)h * D + cc;
   float* lseb = a.lse + ((long long)b * a.H + h) * a.T;
   for (int pass = 0; pass < 32 / RPP; pass += 2) {
     bool ok[2];
@@ -391,7 +393,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const Args a) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       if (!ok[u]) continue;
-      const float inv = 1.f / l[u];
+      const float inv = l[u] > 0.f ? 1.f / l[u] : 0.f;   // l = 0: the row saw no key
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[u][e] *= inv;
       store8f(ob + row[u] * rs, o[u]);
@@ -403,13 +405,81 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const Args a) {
 template <typename T, int D>
 static hipError_t launch_fwd_t(const Args& a, hipStream_t st) {
   using C = FwdCfg<T, D>;
-  const Geo geo{a.layout, a.cp, a.rank, a.T, a.Tkv};
+  const Geo geo{a.layout, a.cp, a.rank, a.T, a.Tkv, a.cu_host, a.ndocs};
   const long long nt = (long long)geo.ntiles(C::BM) * a.B * a.H;
   if (nt == 0) return hipSuccess;
   timing_mark(st);
-  hipLaunchKernelGGL((fwd_kernel<T, D>), dim3((unsigned)nt), dim3(C::NT), 0, st, a);
+  if (a.out_f32)
+    hipLaunchKernelGGL((fwd_kernel<T, D, float>), dim3((unsigned)nt), dim3(C::NT), 0, st, a);
+  else
+    hipLaunchKernelGGL((fwd_kernel<T, D, T>), dim3((unsigned)nt), dim3(C::NT), 0, st, a);
   timing_mark(st);
   return hipGetLastError();
+}
+
+// Ring-step mode: merges the N diagonal blocks into the float32 running state
+// (out_acc, lse_acc) that the chained block-0 ring steps produced (ring_attention
+// page, `_merge_diag`, once per block i = 1..N) and writes the final out in q's
+// dtype and lse. LPR lanes per (b, t, h) row, 8 columns each; an online merge
+// over the blocks in base 2.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void diag_merge_fwd_kernel(const Args a, const float* out_acc,
+                                                             const float* lse_acc) {
+  constexpr int LPR = D / 8;
+  constexpr int GPB = 256 / LPR;
+  using V = typename V8<T>::type;
+  const int tid = threadIdx.x, cc = (tid % LPR) * 8;
+  const long long nrow = (long long)a.B * a.T * a.H;
+  for (long long r = (long long)blockIdx.x * GPB + tid / LPR; r < nrow; r += (long long)gridDim.x * GPB) {
+    const int h = (int)(r % a.H);
+    const long long bt = r / a.H;
+    const int t = (int)(bt % a.T), b = (int)(bt / a.T);
+    const long long qoff = r * D + cc;
+    const long long doff = (long long)b * a.kd_bs + ((long long)t * a.H + h) * D + cc;
+    const long long loff = ((long long)b * a.H + h) * a.T + t;
+    const V qv = load8(reinterpret_cast<const T*>(a.q) + qoff);
+    f32x8 o = *reinterpret_cast<const f32x8*>(out_acc + qoff);
+    float m = lse_acc[loff] * kLog2e;          // state: (m, l = 1, o) or empty
+    float l = m == kNegInf ? 0.f : 1.f;
+    for (int i = 0; i < a.N; ++i) {
+      const long long off = (long long)i * a.kd_blk + doff;
+      const V kv = load8(reinterpret_cast<const T*>(a.kd) + off);
+      const V vv = load8(reinterpret_cast<const T*>(a.vd) + off);
+      const float y = group_sum<LPR>(dot8(qv, kv, 0.f)) * a.c2;
+      const float mn = fmaxf(m, y);
+      const float al = fast_exp2(m - mn), p = fast_exp2(y - mn);
+      l = l * al + p;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = fmaf(p, (float)vv[e], o[e] * al);
+      m = mn;
+    }
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] *= inv;
+    store8f(reinterpret_cast<T*>(a.out) + qoff, o);
+    if ((tid % LPR) == 0) a.lse[loff] = (m + fast_log2(l)) * kLn2;
+  }
+}
+
+template <typename T, int D>
+static hipError_t launch_diag_merge_t(const Args& a, const float* out_acc, const float* lse_acc,
+                                      hipStream_t st) {
+  const long long nrow = (long long)a.B * a.T * a.H;
+  if (nrow == 0) return hipSuccess;
+  constexpr int GPB = 256 / (D / 8);
+  const long long g = (nrow + GPB - 1) / GPB;
+  hipLaunchKernelGGL((diag_merge_fwd_kernel<T, D>), dim3((unsigned)(g < 4096 ? g : 4096)), dim3(256), 0,
+                     st, a, out_acc, lse_acc);
+  return hipGetLastError();
+}
+
+hipError_t launch_diag_merge(const Args& a, const float* out_acc, const float* lse_acc, int dtype, int D,
+                             hipStream_t st) {
+  if (dtype == 0)
+    return D == 128 ? launch_diag_merge_t<bf16, 128>(a, out_acc, lse_acc, st)
+                    : launch_diag_merge_t<bf16, 64>(a, out_acc, lse_acc, st);
+  return D == 128 ? launch_diag_merge_t<float, 128>(a, out_acc, lse_acc, st)
+                  : launch_diag_merge_t<float, 64>(a, out_acc, lse_acc, st);
 }
 
 hipError_t launch_fwd(const Args& a, int dtype, int D, hipStream_t st) {

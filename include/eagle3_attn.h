@@ -52,7 +52,8 @@
  *                        [r*T, (r+1)*T) of S = cp*T; T_kv == S.
  *   E3_LAYOUT_ZIGZAG     zig-zag ring shard (zigzag_ring_attention page, module text):
  *                        S = cp*T is cut into 2*cp chunks of c = T/2; rank r holds chunk r
- *                        then chunk 2*cp-1-r; T_kv == S; B must be 1.
+ *                        then chunk 2*cp-1-r (per document with several documents, see
+ *                        below); T_kv == S; B must be 1.
  *   E3_LAYOUT_HEADSHARD  Ulysses head shard (ulysses_attention page, module text): the full
  *                        sequence for H local heads; T_kv == T; cp is the Ulysses degree and
  *                        T must divide by it (`_scatter_seq_gather_heads`).
@@ -63,8 +64,11 @@
  * Documents: cu_seqlens are GLOBAL document boundaries [num_docs+1] int32 starting at 0
  * and ending at the full sequence length (ulysses_attention page, `cached_ulysses_attention`).
  * num_docs == 0 or 1 means one document. Several documents require B == 1 (varlen tensors
- * are unbatched: zigzag_ring_attention page, `squeeze_batch`) and are not supported with
- * the zig-zag layout (per-document zig-zag halving is not implemented: E3_EUNSUPPORTED).
+ * are unbatched: zigzag_ring_attention page, `squeeze_batch`). With the zig-zag layout
+ * every document is cut into 2*cp chunks (its length must divide by 2*cp) and the share
+ * holds, document after document, chunk rank then chunk 2*cp-1-rank of each (the front
+ * and back half of each local document: zigzag_ring_attention page, `get_half_index`),
+ * so the local document boundaries are cu_seqlens / cp.
  */
 #ifndef EAGLE3_ATTN_H
 #define EAGLE3_ATTN_H
@@ -117,10 +121,11 @@ int eagle3_abi_version(void);
 const char* eagle3_last_error(void);
 
 /* Bytes of device workspace eagle3_attn_bwd / eagle3_shard_bwd need: delta = rowsum(dO*O)
- * and lse*log2(e) (float32 [B, H, P], P = T with each local run, i.e. each of the two
- * zig-zag chunks, padded to a multiple of 64 positions), then, when num_blocks > 1, the
- * block-0 part of dq (float32 [B, T, H, D]). 0 when T == 0. Returns 0 and sets the last
- * error for an invalid problem. */
+ * and lse*log2(e) (float32 [B, H, P]: P = T for one run of local rows; with the zig-zag
+ * layout each chunk of each document is a run, placed at a 16-byte boundary and padded
+ * to 64 rows, P < T + 68 * runs + 128), then, when num_blocks > 1, the block-0 part of
+ * dq (float32 [B, T, H, D]). 0 when T == 0. Returns 0 and sets the last error for an
+ * invalid problem. */
 size_t eagle3_bwd_workspace_bytes(const e3_problem* p);
 
 /* Forward of the full sequence (layout FULL or HEADSHARD):
@@ -168,11 +173,13 @@ int lse_merge(float* out, float* lse, const float* block_out, const float* block
 /* ---- Measurement hook ---------------------------------------------------------------- */
 
 /* While `events` is non-NULL, every compute entry point called on this thread records
- * events[0] on its stream before its first kernel and events[k+1] after its k-th stage
- * (at most `capacity` events; the forward has 1 stage, the attention kernel; the
- * backward 3: dQ (which also writes delta and lse*log2(e)), dK/dV, and the wait for the
- * side stream's diagonal-block gradients). The caller creates and owns the events; NULL stops
- * recording. Returns E3_OK. */
+ * events[0] on its stream before its first kernel and then one event after each stage
+ * (at most `capacity` events). Forward: events[1] after the attention kernel.
+ * Backward: events[1] after dQ (which also writes delta and lse*log2(e)); events[2] and
+ * events[3] on the side stream just before and after the diagonal-block gradients
+ * (on the caller's stream, with nothing between them, when num_blocks == 1);
+ * events[4] after dK/dV; events[5] after the caller's stream has joined the side
+ * stream. The caller creates and owns the events; NULL stops recording. Returns E3_OK. */
 int eagle3_set_timing_events(hipEvent_t* events, int capacity);
 
 /* Number of events recorded by the last compute entry point called on this thread. */

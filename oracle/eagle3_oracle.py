@@ -53,7 +53,7 @@ LAYOUTS = ("full", "contiguous", "zigzag", "headshard")
 # Layout: global positions of the local query rows, document starts, masks
 # ---------------------------------------------------------------------------
 
-def query_positions(layout: str, T: int, cp: int = 1, rank: int = 0) -> np.ndarray:
+def query_positions(layout: str, T: int, cp: int = 1, rank: int = 0, cu_seqlens=None) -> np.ndarray:
     """Global sequence position of each local query row.
 
     full / headshard: the whole sequence is local (ulysses_attention page,
@@ -61,9 +61,13 @@ def query_positions(layout: str, T: int, cp: int = 1, rank: int = 0) -> np.ndarr
       subset of heads).
     contiguous: rank r holds positions [r*T, (r+1)*T) (ring_attention page,
       module text: each rank holds a contiguous shard S/cp).
-    zigzag: the sequence is cut into 2*cp chunks of c = T/2; rank r holds chunk
-      r (early) then chunk 2*cp-1-r (late) (zigzag_ring_attention page, module
-      text; ring_attention page, `_CachedZigZagRingAttention`).
+    zigzag: every document is cut into 2*cp chunks; rank r holds chunk r
+      (early) then chunk 2*cp-1-r (late) of each document, documents one after
+      the other (zigzag_ring_attention page, module text: the 2*cp chunks and
+      their ownership; `get_half_index`: the front and back half of EACH varlen
+      document; ring_attention page, `_CachedZigZagRingAttention`). With one
+      document (cu_seqlens None) the chunks are c = T/2 rows of the sequence
+      S = cp*T. Every document length must divide by 2*cp.
     """
     if layout in ("full", "headshard"):
         return np.arange(T, dtype=np.int64)
@@ -71,10 +75,20 @@ def query_positions(layout: str, T: int, cp: int = 1, rank: int = 0) -> np.ndarr
         return rank * T + np.arange(T, dtype=np.int64)
     if layout == "zigzag":
         assert T % 2 == 0
-        c = T // 2
-        early = rank * c + np.arange(c, dtype=np.int64)
-        late = (2 * cp - 1 - rank) * c + np.arange(c, dtype=np.int64)
-        return np.concatenate([early, late])
+        S = cp * T
+        if cu_seqlens is None:
+            bounds = [(0, S)]
+        else:
+            cu = [int(x) for x in cu_seqlens]
+            assert cu[0] == 0 and cu[-1] == S
+            bounds = list(zip(cu[:-1], cu[1:]))
+        parts = []
+        for lo, hi in bounds:
+            assert (hi - lo) % (2 * cp) == 0, "document length must divide by 2*cp"
+            c = (hi - lo) // (2 * cp)
+            parts.append(lo + rank * c + np.arange(c, dtype=np.int64))
+            parts.append(lo + (2 * cp - 1 - rank) * c + np.arange(c, dtype=np.int64))
+        return np.concatenate(parts) if parts else np.zeros(0, dtype=np.int64)
     raise ValueError(layout)
 
 
@@ -103,7 +117,7 @@ def visible_mask(qpos: np.ndarray, kpos: np.ndarray, cu_seqlens=None) -> np.ndar
 def pair_count(layout: str, T: int, cp: int = 1, rank: int = 0, cu_seqlens=None) -> int:
     """Number of attended block-0 (query, key) pairs of one share, counted
     row by row from the visibility rule."""
-    qpos = query_positions(layout, T, cp, rank)
+    qpos = query_positions(layout, T, cp, rank, cu_seqlens)
     lo = doc_start(cu_seqlens, qpos)
     return int(np.sum(qpos - lo + 1))
 
@@ -189,7 +203,7 @@ def forward(q, k0, v0, kd, vd, scale, cu_seqlens=None, layout="full", cp=1, rank
     q = np.asarray(q, np.float64)
     B, T, H, D = q.shape
     hs = _heads(H, heads)
-    qpos = query_positions(layout, T, cp, rank)
+    qpos = query_positions(layout, T, cp, rank, cu_seqlens)
     out = np.zeros((B, T, len(hs), D))
     lse = np.zeros((B, len(hs), T))
     for b in range(B):
@@ -270,7 +284,7 @@ def backward(dout, q, k0, v0, kd, vd, scale, cu_seqlens=None, layout="full", cp=
     vd = np.asarray(vd)
     dout = np.asarray(dout)
     hs = _heads(H, heads)
-    qpos = query_positions(layout, T, cp, rank)
+    qpos = query_positions(layout, T, cp, rank, cu_seqlens)
     Tkv = k0.shape[1]
     N = kd.shape[1]
     dq = np.zeros((B, T, len(hs), D))

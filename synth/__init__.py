@@ -190,35 +190,45 @@ def local_chunks(w: Workload, cp: Optional[int] = None, rank: Optional[int] = No
 
 def make_inputs(w: Workload, device="cpu", with_dout: bool = True,
                 cp: Optional[int] = None, rank: Optional[int] = None,
-                layout: Optional[str] = None) -> dict:
+                layout: Optional[str] = None, positions=None) -> dict:
     """All inputs of one share:
          q    [B, T, H, D]
          k0,v0 [B, S, H, D]         (block 0, full sequence in global order)
          kd,vd [B, N, T, H, D]      (blocks 1..N, local rows)
          dout [B, T, H, D]
-    """
+    The local rows are the share's generator chunks, or, when `positions` (the
+    global position of every local row, in local order) is given, those rows of
+    the virtual global tensors; a zig-zag share of several documents needs them."""
     layout = layout or w.layout
-    loc = local_chunks(w, cp, rank, layout)
     allc = list(range(w.S // w.gen_chunk()))
+    if positions is None:
+        if layout == "zigzag" and w.doc_lens is not None and len(w.doc_lens) > 1:
+            raise ValueError("a zig-zag share of several documents needs the positions of its rows")
+        loc = local_chunks(w, cp, rank, layout)
+        pick = lambda t: t
+    else:
+        loc = allc
+        idx = torch.as_tensor(np.asarray(positions, dtype=np.int64))
+        pick = lambda t: t.index_select(0, idx)
     out = {}
 
     def stack_b(fn):
         return torch.stack([fn(b) for b in range(w.B)], 0)
 
-    out["q"] = stack_b(lambda b: global_rows(w, "q", 0, b, loc))
+    out["q"] = stack_b(lambda b: pick(global_rows(w, "q", 0, b, loc)))
     out["k0"] = stack_b(lambda b: global_rows(w, "k", 0, b, allc))
     out["v0"] = stack_b(lambda b: global_rows(w, "v", 0, b, allc))
     if w.N > 0:
         out["kd"] = stack_b(lambda b: torch.stack(
-            [global_rows(w, "k", i, b, loc) for i in range(1, w.num_blocks)], 0))
+            [pick(global_rows(w, "k", i, b, loc)) for i in range(1, w.num_blocks)], 0))
         out["vd"] = stack_b(lambda b: torch.stack(
-            [global_rows(w, "v", i, b, loc) for i in range(1, w.num_blocks)], 0))
+            [pick(global_rows(w, "v", i, b, loc)) for i in range(1, w.num_blocks)], 0))
     else:
         T = out["q"].shape[1]
         out["kd"] = torch.zeros(w.B, 0, T, w.H, w.D, dtype=w.torch_dtype)
         out["vd"] = torch.zeros(w.B, 0, T, w.H, w.D, dtype=w.torch_dtype)
     if with_dout:
-        out["dout"] = stack_b(lambda b: global_rows(w, "dout", 0, b, loc))
+        out["dout"] = stack_b(lambda b: pick(global_rows(w, "dout", 0, b, loc)))
     if device != "cpu":
         out = {k: v.to(device) for k, v in out.items()}
     return out

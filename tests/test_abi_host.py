@@ -54,7 +54,13 @@ BAD = [
     (dict(cu_seqlens=[1, 100, 256]), e3.E3_EINVAL, "must be 0"),
     (dict(cu_seqlens=[0, 200, 100, 256]), e3.E3_EINVAL, "non-decreasing"),
     (dict(cu_seqlens=[0, 100, 256], B=2), e3.E3_EINVAL, "B == 1"),
-    (dict(layout="zigzag", cp=2, T=256, T_kv=512, cu_seqlens=[0, 100, 512]), e3.E3_EUNSUPPORTED, "ZIGZAG"),
+    # zig-zag documents are each cut into 2cp chunks: lengths must divide by 2cp
+    (dict(layout="zigzag", cp=2, T=256, T_kv=512, cu_seqlens=[0, 102, 512]), e3.E3_EINVAL, "multiple of 2*cp"),
+    # strides under which batch rows or blocks would overlap (gradients are written through them)
+    (dict(B=2, k0_batch_stride=256 * 2 * 128 - 8), e3.E3_EINVAL, "k0_batch_stride"),
+    (dict(kd_block_stride=256 * 2 * 128 - 8), e3.E3_EINVAL, "kd_block_stride"),
+    (dict(B=2, kd_batch_stride=2 * 256 * 2 * 128 - 8), e3.E3_EINVAL, "kd_batch_stride"),
+    (dict(k0_batch_stride=12), e3.E3_EINVAL, "multiples of 8"),
 ]
 
 
@@ -109,8 +115,10 @@ def test_workspace_bytes():
     assert p.workspace_bytes() == 2 * 1 * 3 * P * 4 + 1 * 1000 * 3 * 128 * 4
     assert prob(B=1, T=1000, T_kv=1000, H=3, num_blocks=1).workspace_bytes() == 2 * 3 * P * 4
     # zig-zag: each of the two local chunks is padded to 64 rows on its own
+    # zig-zag: run i (of 150 rows) starts at roundup4(local start) + 68 i: 0 and
+    # 152 + 68 = 220, and ends its padding at 220 + 192 = 412, rounded up to 448
     zz = e3.Problem(1, 300, 3 * 300, 3, 128, 3, 0.1, layout="zigzag", cp=3, rank=2)
-    Pz = 2 * 192
+    Pz = 448
     assert zz.workspace_bytes() == 2 * 3 * Pz * 4 + 300 * 3 * 128 * 4
 
 
@@ -124,6 +132,10 @@ SHARES = [
     ("zigzag", 256, 4, 1, None),
     ("zigzag", 300, 3, 2, None),     # chunk 150: ragged tiles
     ("zigzag", 16384, 8, 3, None),   # the zig-zag workload's geometry
+    # several documents, each cut into 2cp chunks (one empty, one of a single chunk row)
+    ("zigzag", 256, 4, 1, [0, 8, 400, 400, 1024]),
+    ("zigzag", 2048, 8, 3, [0, 4096, 4112, 12288, 16384]),
+    ("zigzag", 90, 3, 0, [0, 30, 36, 270]),
 ]
 
 
@@ -138,7 +150,7 @@ def test_shard_driver_positions_and_pair_counts(layout, T, cp, rank, cu):
     p = share_problem(layout, T, cp, rank, cu)
     pos = p.query_positions()
     ocp = cp if layout in ("contiguous", "zigzag") else 1
-    np.testing.assert_array_equal(pos, oracle.query_positions(layout, T, ocp, rank))
+    np.testing.assert_array_equal(pos, oracle.query_positions(layout, T, ocp, rank, cu))
     assert p.pair_count() == oracle.pair_count(layout, T, ocp, rank, cu)
 
 
@@ -149,7 +161,7 @@ def test_shard_driver_key_tiles_cover_exactly_the_visible_keys(layout, T, cp, ra
     of their query tile; the tiles of a segment follow the ring order."""
     p = share_problem(layout, T, cp, rank, cu)
     ocp = cp if layout in ("contiguous", "zigzag") else 1
-    qpos = oracle.query_positions(layout, T, ocp, rank)
+    qpos = oracle.query_positions(layout, T, ocp, rank, cu)
     lo = oracle.doc_start(cu, qpos)
     ntiles, BM = p.fwd_tiles()
     covered = np.zeros(T, dtype=bool)
@@ -180,10 +192,15 @@ def test_shard_driver_key_tiles_cover_exactly_the_visible_keys(layout, T, cp, ra
         heavy.append(int(g[0]))
         if layout in ("contiguous", "zigzag"):
             # the visited K/V chunks follow the ring: step j holds rank (r - j) mod cp
+            # (zig-zag: chunks of the tile's document, 2cp of them)
+            dlo = 0
             c = T if layout == "contiguous" else T // 2
+            if layout == "zigzag" and cu is not None:
+                d = int(np.searchsorted(cu, g[0], side="right")) - 1
+                dlo, c = int(cu[d]), (int(cu[d + 1]) - int(cu[d])) // (2 * ocp)
             order = []
             for (s0, _, _) in segs:
-                ch = s0 // c
+                ch = (s0 - dlo) // c
                 src = ch if ch < ocp else 2 * ocp - 1 - ch
                 if not order or order[-1] != src:
                     order.append(src)
@@ -204,3 +221,23 @@ def test_workload_pair_counts_match_golden():
         p = e3.Problem(w.B, w.T, w.T_kv, w.H, w.D, w.num_blocks, w.scale, dtype=dt,
                        layout=w.layout, cp=w.cp, rank=w.rank, cu_seqlens=w.cu_seqlens())
         assert p.pair_count() == g[name]["P0"], name
+
+
+def test_binding_checks_strides_against_the_problem():
+    """The binding compares every k/v tensor's strides with the Problem's before
+    calling the library (nothing is launched: it raises first)."""
+    B, nb, T, H, D = 2, 3, 64, 2, 64
+    cache = torch.zeros(B, nb, T, H, D)
+    dense = e3.Problem(B, T, T, H, D, nb, 0.125, dtype=torch.float32)
+    q = torch.zeros(B, T, H, D)
+    with pytest.raises(ValueError, match="strides"):
+        e3.fwd(dense, q, cache[:, 0], cache[:, 0], cache[:, 1:], cache[:, 1:])
+    blk = nb * T * H * D
+    strided = e3.Problem(B, T, T, H, D, nb, 0.125, dtype=torch.float32, k0_batch_stride=blk,
+                         kd_batch_stride=blk, kd_block_stride=T * H * D)
+    with pytest.raises(ValueError, match="strides"):
+        e3.fwd(strided, q, cache[:, 0].contiguous(), cache[:, 0], cache[:, 1:], cache[:, 1:])
+    assert strided.k0_strides == (blk, H * D, D, 1)
+    assert strided.kd_strides == (blk, T * H * D, H * D, D, 1)
+    g = e3._strided_empty((B, nb - 1, T, H, D), strided.kd_strides, torch.float32, "cpu")
+    assert g.stride() == strided.kd_strides

@@ -7,11 +7,11 @@ import random
 import pytest
 
 import synth
-from tests.parity import assert_within, compare, run_hip, run_oracle, say
+from tests.parity import assert_within, compare, inputs, run_hip, run_oracle, say
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 24
+N_CASES = 32
 
 
 def _docs(rng, total):
@@ -24,7 +24,28 @@ def _docs(rng, total):
     return lens
 
 
+def _zigzag_docs(rng, cp, ndocs):
+    """Document lengths that are multiples of 2cp (some empty, some one chunk row)."""
+    return [2 * cp * rng.choice([0, 1, rng.randint(1, 8), rng.randint(5, 60)]) for _ in range(ndocs)]
+
+
+def fuzz_case_docs(i):
+    """Cases 24..31: zig-zag shares of several documents, every degree and rank."""
+    rng = random.Random(5000 + i)
+    dtype = "f32" if i % 4 == 3 else "bf16"
+    D = rng.choice([64, 128])
+    cp = rng.randint(1, 4)
+    lens = _zigzag_docs(rng, cp, rng.randint(2, 6))
+    if sum(lens) == 0:
+        lens[0] = 2 * cp
+    return synth.small_workload(f"fuzz{i}", dtype=dtype, D=D, H=rng.randint(1, 4),
+                                num_blocks=rng.randint(1, 9), seed=i, layout="zigzag",
+                                S=sum(lens), cp=cp, rank=rng.randrange(cp), doc_lens=lens)
+
+
 def fuzz_case(i):
+    if i >= 24:
+        return fuzz_case_docs(i)
     rng = random.Random(1000 + i)
     dtype = "f32" if i % 4 == 3 else "bf16"
     D = rng.choice([64, 128])
@@ -59,7 +80,7 @@ def fuzz_case(i):
 def test_fuzz_parity(i):
     w = fuzz_case(i)
     say(f"[fuzz] {i}: {w}")
-    inp = synth.make_inputs(w)
+    inp = inputs(w)
     hip = run_hip(w, inp)
     ref = run_oracle(w, inp)
     m = compare(w, hip, ref)

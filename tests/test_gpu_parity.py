@@ -9,7 +9,7 @@ import torch
 import eagle_draft_amd as e3
 import oracle
 import synth
-from tests.parity import assert_within, compare, run_hip, run_oracle, say
+from tests.parity import assert_within, compare, inputs, run_hip, run_oracle, say
 
 pytestmark = pytest.mark.gpu
 
@@ -39,6 +39,15 @@ CASES = {
     "bf16_single_row": W(S=1, H=2, D=128, num_blocks=3),
     "f32_two_rows_d64": W(dtype="f32", S=2, H=1, D=64, num_blocks=2),
     "zigzag_one_row_chunks": W(S=8, H=1, D=128, num_blocks=2, layout="zigzag", cp=4, rank=2),
+    # several documents, each cut into 2cp chunks (an empty one, one of one-row chunks)
+    "zigzag_docs_cp4": W(S=1024, H=2, D=128, num_blocks=3, layout="zigzag", cp=4, rank=1,
+                         doc_lens=[8, 400, 0, 616]),
+    "zigzag_docs_r3_cp8": W(S=4096, H=2, D=128, num_blocks=8, layout="zigzag", cp=8, rank=3,
+                            doc_lens=[1024, 16, 2048, 1008]),
+    "zigzag_docs_d64": W(S=960, H=2, D=64, num_blocks=4, layout="zigzag", cp=2, rank=1,
+                         doc_lens=[260, 4, 696]),
+    "zigzag_docs_f32": W(dtype="f32", S=480, H=2, D=64, num_blocks=3, layout="zigzag", cp=3,
+                         rank=2, doc_lens=[60, 6, 414]),
 }
 
 
@@ -46,12 +55,28 @@ CASES = {
 def test_parity_small(name):
     w = CASES[name]
     say(f"[parity] {name}: {w}")
-    inp = synth.make_inputs(w)
+    inp = inputs(w)
     hip = run_hip(w, inp)
     ref = run_oracle(w, inp)
     m = compare(w, hip, ref)
     say(f"[parity] {name}: {m}")
     assert_within(w, m)
+
+
+def test_unseen_keys_of_a_multi_document_zigzag_share_get_exact_zero_grads():
+    """In every document, the chunks after the share's late chunk are seen by no
+    local query (the oracle's visibility rule names them)."""
+    w = CASES["zigzag_docs_r3_cp8"]
+    inp = inputs(w)
+    _, _, (dq, dk0, dv0, dkd, dvd) = run_hip(w, inp)
+    cu = w.cu_seqlens()
+    qpos = oracle.query_positions("zigzag", w.T, w.cp, w.rank, cu)
+    seen = oracle.visible_mask(qpos, np.arange(w.S), cu).any(axis=0)
+    unseen = torch.from_numpy(np.nonzero(~seen)[0])
+    assert len(unseen) > 0
+    assert torch.count_nonzero(dk0[:, unseen]) == 0
+    assert torch.count_nonzero(dv0[:, unseen]) == 0
+    assert torch.count_nonzero(dk0[:, torch.from_numpy(np.nonzero(seen)[0])]) > 0
 
 
 def test_unseen_keys_get_exact_zero_grads():

@@ -4,9 +4,12 @@ dense, packed varlen, Ulysses head share and zig-zag ring rank 3 of cp=8.
 
 Every head is compared with the oracle element by element, except for the
 zig-zag share, where two heads (0 and 21) are compared in full -- each costs
-about 1.07e9 attended pairs on the host -- and all 32 heads are checked for
-the properties that hold at any size (finite outputs, exact zeros for the K/V
-rows no local query sees, the softmax bounds of lse)."""
+about 1.07e9 attended pairs on the host -- and, for all 32 heads, the per-row
+outputs (out, lse, dq, dkd, dvd) are compared on a sample of rows (the starts,
+middles and ends of both chunks, the rows around query-tile edges and seeded
+random rows), whose oracle values need only those rows' score rows. All heads
+are also checked for the properties that hold at any size (finite outputs, exact
+zeros for the K/V rows no local query sees, the softmax bounds of lse)."""
 import math
 
 import numpy as np
@@ -15,7 +18,7 @@ import torch
 
 import oracle
 import synth
-from tests.parity import assert_within, compare, run_hip, run_oracle, say
+from tests.parity import TOL, assert_within, compare, rel, run_hip, run_oracle, say, stored_out
 
 pytestmark = pytest.mark.gpu
 
@@ -66,3 +69,65 @@ def test_workload_parity_full_size(name, heads):
     say(f"[workload] {name}: {m}")
     assert_within(w, m)
     inp_cache.clear()
+
+
+def sample_rows(w, n_random=16, seed=0):
+    """Row sample of a share: the first, middle and last rows of each run (the
+    zig-zag chunks), the rows on both sides of 64- and 128-row tile edges, and
+    seeded random rows."""
+    c = w.T // 2 if w.layout == "zigzag" else w.T
+    rows = set()
+    for r0 in range(0, w.T, c):
+        for o in (0, 1, 2, 63, 64, 127, 128, 129, c // 2 - 1, c // 2, c - 129, c - 128, c - 65,
+                  c - 64, c - 2, c - 1):
+            if 0 <= o < c:
+                rows.add(r0 + o)
+    rng = np.random.default_rng(seed)
+    rows.update(int(x) for x in rng.integers(0, w.T, n_random))
+    return np.array(sorted(rows))
+
+
+def oracle_rows(w, inp, rows):
+    """Oracle out, lse, dq, dkd, dvd of the sampled rows for every head; a row's
+    values depend only on its own score row, so the oracle runs on those rows
+    alone (their global positions passed explicitly)."""
+    cu = w.cu_seqlens()
+    qpos = oracle.query_positions(w.layout, w.T, w.cp, w.rank, cu)[rows.numpy()]
+    f = lambda t: t.double().numpy()
+    res = {k: [] for k in ("out", "lse", "dq", "dkd", "dvd")}
+    for h in range(w.H):
+        q, do = f(inp["q"][0, rows, h]), f(inp["dout"][0, rows, h])
+        k0, v0 = f(inp["k0"][0, :, h]), f(inp["v0"][0, :, h])
+        kd, vd = f(inp["kd"][0][:, rows][:, :, h]), f(inp["vd"][0][:, rows][:, :, h])
+        o, l = oracle.forward_head(q, k0, v0, kd, vd, w.scale, qpos, cu, rows=len(rows))
+        dq, _, _, dkd, dvd = oracle.backward_head(do, q, k0, v0, kd, vd, w.scale, qpos, cu,
+                                                  out=stored_out(w, o), lse=l, rows=len(rows))
+        for k, v in (("out", o), ("lse", l), ("dq", dq), ("dkd", dkd), ("dvd", dvd)):
+            res[k].append(v)
+    return res
+
+
+@pytest.mark.timeout(900)
+def test_zigzag_share_all_heads_on_sampled_rows():
+    w = synth.workload("zigzag")
+    say(f"[workload] zigzag row sample: generating inputs {w}")
+    inp = synth.make_inputs(w)
+    say("[workload] zigzag row sample: HIP forward + backward")
+    out, lse, (dq, dk0, dv0, dkd, dvd) = run_hip(w, inp)
+    del dk0, dv0
+    rows = torch.from_numpy(sample_rows(w))
+    say(f"[workload] zigzag row sample: oracle on {len(rows)} rows x {w.H} heads")
+    ref = oracle_rows(w, inp, rows)
+    t = TOL[w.dtype]
+    f = lambda x: x.double().numpy()
+    m = {"out": 0.0, "lse": 0.0, "dq": 0.0, "dkd": 0.0, "dvd": 0.0}
+    for h in range(w.H):
+        m["out"] = max(m["out"], float(np.abs(f(out[0, rows, h]) - ref["out"][h]).max()))
+        m["lse"] = max(m["lse"], float(np.abs(f(lse[0, h, rows]) - ref["lse"][h]).max()))
+        m["dq"] = max(m["dq"], rel(f(dq[0, rows, h]), ref["dq"][h]))
+        m["dkd"] = max(m["dkd"], rel(f(dkd[0][:, rows][:, :, h]), ref["dkd"][h]))
+        m["dvd"] = max(m["dvd"], rel(f(dvd[0][:, rows][:, :, h]), ref["dvd"][h]))
+    say(f"[workload] zigzag row sample (worst head): {m}")
+    assert m["out"] <= t["out"] and m["lse"] <= t["lse"], m
+    for k in ("dq", "dkd", "dvd"):
+        assert m[k] <= t["grad"], (k, m)

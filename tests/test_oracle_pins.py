@@ -85,6 +85,8 @@ CASES = [
     ("contiguous", 8, 3, 2, [10, 14], 3, 1),
     ("zigzag", 8, 2, 1, None, 3, 1),
     ("zigzag", 6, 3, 0, None, 2, 1),
+    ("zigzag", 12, 2, 1, [8, 16], 3, 1),          # each document cut into 2cp chunks
+    ("zigzag", 12, 3, 2, [6, 0, 12, 18], 2, 1),
     ("headshard", 16, 2, 0, [9, 7], 3, 1),
 ]
 
@@ -102,7 +104,7 @@ def test_oracle_matches_sdpa_augmented_mask(layout, T, cp, rank, doc_lens, nb, B
     S = T * cp if layout in ("contiguous", "zigzag") else T
     p = rand_problem(rng, B=B, T=T, Tkv=S, nb=nb)
     docs, cu = _docs_and_cu(S, doc_lens)
-    qpos = oracle.query_positions(layout, T, cp, rank)
+    qpos = oracle.query_positions(layout, T, cp, rank, cu)
     ref = sdpa_reference(p, qpos, docs)
     out, lse = oracle.forward(p["q"], p["k0"], p["v0"], p["kd"], p["vd"], p["scale"], cu,
                               layout, cp, rank, rows=5)
@@ -325,30 +327,33 @@ def test_merge_special_cases():
 # Layouts: shares re-assembled equal the full-sequence result
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("layout", ["contiguous", "zigzag"])
-def test_ring_layout_shares_reassemble_to_full(layout):
+@pytest.mark.parametrize("layout,doc_lens", [("contiguous", None), ("zigzag", None),
+                                             ("contiguous", [5, 20, 7]),
+                                             ("zigzag", [8, 0, 16, 8])])
+def test_ring_layout_shares_reassemble_to_full(layout, doc_lens):
     rng = np.random.default_rng(11)
     cp, S, H, D, nb = 4, 32, 2, 8, 3
     T = S // cp
+    _, cu = _docs_and_cu(S, doc_lens)
     full = rand_problem(rng, T=S, H=H, D=D, nb=nb)
     f_out, f_lse = oracle.forward(full["q"], full["k0"], full["v0"], full["kd"], full["vd"],
-                                  full["scale"])
+                                  full["scale"], cu)
     f_grads = oracle.backward(full["dout"], full["q"], full["k0"], full["v0"], full["kd"],
-                              full["vd"], full["scale"])
+                              full["vd"], full["scale"], cu)
     dk0 = np.zeros_like(f_grads[1])
     dv0 = np.zeros_like(f_grads[2])
     seen = np.zeros(S, dtype=int)
     for r in range(cp):
-        pos = oracle.query_positions(layout, T, cp, r)
+        pos = oracle.query_positions(layout, T, cp, r, cu)
         seen[pos] += 1
         sh = {k: full[k][:, pos] for k in ("q", "dout")}
         sh.update({k: full[k][:, :, pos] for k in ("kd", "vd")})
         out, lse = oracle.forward(sh["q"], full["k0"], full["v0"], sh["kd"], sh["vd"],
-                                  full["scale"], None, layout, cp, r)
+                                  full["scale"], cu, layout, cp, r)
         np.testing.assert_allclose(out, f_out[:, pos], atol=1e-12)
         np.testing.assert_allclose(lse, f_lse[:, :, pos], atol=1e-12)
         dq, a, b, dkd, dvd = oracle.backward(sh["dout"], sh["q"], full["k0"], full["v0"], sh["kd"],
-                                             sh["vd"], full["scale"], None, layout, cp, r)
+                                             sh["vd"], full["scale"], cu, layout, cp, r)
         np.testing.assert_allclose(dq, f_grads[0][:, pos], atol=1e-12)
         np.testing.assert_allclose(dkd, f_grads[3][:, :, pos], atol=1e-12)
         np.testing.assert_allclose(dvd, f_grads[4][:, :, pos], atol=1e-12)
@@ -402,6 +407,39 @@ def test_zigzag_every_rank_does_equal_work(cp, c):
         assert oracle.visible_mask(qpos, np.arange(S)).sum() == counts[r]
 
 
+@pytest.mark.parametrize("cp,doc_lens", [(2, [4, 12, 0, 8]), (4, [8, 24, 96]), (8, [16, 4096, 32])])
+def test_zigzag_several_documents_equal_work_and_halves(cp, doc_lens):
+    """Several documents (zigzag_ring_attention page, `get_half_index`: the front
+    and back half of each varlen document): every rank does equal causal work in
+    every document (the page's load-balance statement, per document: 2cp*c^2 + c
+    pairs for chunks of c), the shares partition the sequence, and each local
+    document is [front half | back half] with every front position before every
+    back position; local documents follow the global order with local
+    boundaries cu / cp."""
+    S = sum(doc_lens)
+    T = S // cp
+    cu = np.concatenate([[0], np.cumsum(doc_lens)]).astype(np.int32)
+    seen = np.zeros(S, dtype=int)
+    want = sum(2 * cp * (L // (2 * cp)) ** 2 + L // (2 * cp) for L in doc_lens)
+    for r in range(cp):
+        qpos = oracle.query_positions("zigzag", T, cp, r, cu)
+        seen[qpos] += 1
+        assert oracle.pair_count("zigzag", T, cp, r, cu) == want
+        vis = oracle.visible_mask(qpos, np.arange(S), cu)
+        assert vis.sum() == want                                  # brute force from the mask
+        for d, L in enumerate(doc_lens):
+            a, b = cu[d] // cp, cu[d + 1] // cp                    # local document d
+            loc = qpos[a:b]
+            assert np.all((loc >= cu[d]) & (loc < cu[d + 1]))
+            front, back = loc[: (b - a) // 2], loc[(b - a) // 2:]
+            if len(front):
+                assert front.max() < back.min()
+                assert np.all(np.diff(front) == 1) and np.all(np.diff(back) == 1)
+    assert np.all(seen == 1)
+    assert sum(oracle.pair_count("zigzag", T, cp, r, cu) for r in range(cp)) == \
+        sum(L * (L + 1) // 2 for L in doc_lens)
+
+
 @pytest.mark.parametrize("cp,L", [(2, 4), (8, 16), (8, 1024)])
 def test_contiguous_last_rank_does_about_twice_the_mean(cp, L):
     # ring_attention page, `_CachedZigZagRingAttention`: a contiguous shard
@@ -442,6 +480,29 @@ def test_ring_order_and_per_step_visibility():
             assert front.all() and not back.any()
         else:            # only the late rows see the block, all of it
             assert not early.any() and late.all()
+    # the same rule inside every document of a packed sequence ("front/back half
+    # uses the halved cu_seqlens": zigzag_ring_attention page, `_block_forward`)
+    doc_lens = [16, 32, 8]
+    cu = np.concatenate([[0], np.cumsum(doc_lens)]).astype(np.int32)
+    S = int(cu[-1])
+    qpos = oracle.query_positions("zigzag", S // cp, cp, r, cu)
+    for d, L in enumerate(doc_lens):
+        c = L // (2 * cp)
+        rows = qpos[cu[d] // cp: cu[d + 1] // cp]
+        for src, chunks in oracle.ring_steps("zigzag", cp, r):
+            keys = np.concatenate([cu[d] + np.arange(ch * c, (ch + 1) * c) for ch in chunks])
+            vis = oracle.visible_mask(rows, keys, cu)
+            early, late = vis[:c], vis[c:]
+            if src == r:
+                assert early[:, :c].sum() == c * (c + 1) // 2 and not early[:, c:].any()
+                assert late[:, :c].all() and late[:, c:].sum() == c * (c + 1) // 2
+            elif src < r:
+                assert vis[:, :c].all() and not vis[:, c:].any()
+            else:
+                assert not early.any() and late.all()
+            # keys of other documents are never visible to these rows
+            other = np.setdiff1d(np.arange(S), np.arange(cu[d], cu[d + 1]))
+            assert not oracle.visible_mask(rows, other, cu).any()
 
 
 # ---------------------------------------------------------------------------

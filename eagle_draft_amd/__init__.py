@@ -27,7 +27,7 @@ import torch  # loaded first: the library then shares torch's HIP runtime
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libeagle3_attn.so")
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 E3_OK, E3_EINVAL, E3_EUNSUPPORTED, E3_EHIP = 0, -1, -2, -3
 LAYOUTS = {"full": 0, "contiguous": 1, "zigzag": 2, "headshard": 3}
@@ -49,7 +49,7 @@ class _Problem(ctypes.Structure):
         ("cu_seqlens_host", ctypes.POINTER(ctypes.c_int32)),
         ("cu_seqlens_dev", ctypes.c_void_p),
         ("k0_batch_stride", ctypes.c_int64), ("kd_batch_stride", ctypes.c_int64),
-        ("kd_block_stride", ctypes.c_int64),
+        ("kd_block_stride", ctypes.c_int64), ("deterministic", ctypes.c_int32),
     ]
 
 
@@ -91,6 +91,24 @@ def _load():
     lib.eagle3_fwd_tile_segments.argtypes = [P, ctypes.c_int, ctypes.POINTER(ctypes.c_int32),
                                              ctypes.POINTER(ctypes.c_int32), ctypes.c_int]
     lib.eagle3_fwd_tile_segments.restype = ctypes.c_int
+    for name in ("eagle3_ulysses_seq_to_head", "eagle3_ulysses_head_to_seq"):
+        f = getattr(lib, name)
+        f.argtypes = [ctypes.c_int] * 7 + [vp, vp, vp]
+        f.restype = ctypes.c_int
+    for name in ("eagle3_ulysses_lse_gather", "eagle3_ulysses_lse_scatter"):
+        f = getattr(lib, name)
+        f.argtypes = [ctypes.c_int] * 5 + [vp, vp, vp]
+        f.restype = ctypes.c_int
+    lib.eagle3_target_cp_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp]
+    lib.eagle3_target_cp_fwd.restype = ctypes.c_int
+    lib.eagle3_ring_fwd_step.argtypes = [P, ctypes.c_int, vp, vp, vp, vp, vp, vp]
+    lib.eagle3_ring_fwd_step.restype = ctypes.c_int
+    lib.eagle3_diag_merge_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.eagle3_diag_merge_fwd.restype = ctypes.c_int
+    lib.eagle3_ring_bwd_step.argtypes = [P, ctypes.c_int] + [vp] * 10 + [vp]
+    lib.eagle3_ring_bwd_step.restype = ctypes.c_int
+    lib.eagle3_diag_bwd.argtypes = [P] + [vp] * 10 + [vp]
+    lib.eagle3_diag_bwd.restype = ctypes.c_int
     lib.eagle3_set_timing_events.argtypes = [vp, ctypes.c_int]
     lib.eagle3_set_timing_events.restype = ctypes.c_int
     lib.eagle3_timing_events_recorded.restype = ctypes.c_int
@@ -125,7 +143,7 @@ class Problem:
     def __init__(self, B: int, T: int, T_kv: int, H: int, D: int, num_blocks: int, scale: float,
                  dtype=torch.bfloat16, layout: str = "full", cp: int = 1, rank: int = 0,
                  cu_seqlens=None, device=None, k0_batch_stride: int = 0,
-                 kd_batch_stride: int = 0, kd_block_stride: int = 0):
+                 kd_batch_stride: int = 0, kd_block_stride: int = 0, deterministic: bool = False):
         if dtype not in DTYPES:
             raise ValueError(f"dtype {dtype} not supported (bfloat16 or float32)")
         if layout not in LAYOUTS:
@@ -163,6 +181,8 @@ class Problem:
         s.k0_batch_stride = k0_batch_stride
         s.kd_batch_stride = kd_batch_stride
         s.kd_block_stride = kd_block_stride
+        s.deterministic = 1 if deterministic else 0
+        self.deterministic = bool(deterministic)
         self._s = s
         # Element strides of the k/v tensors (block 0 and the diagonal blocks) and
         # of their gradients; 0 in the arguments means dense.
@@ -325,6 +345,165 @@ def lse_merge(out, lse, block_out, block_lse, block_lse_layout: int = 0):
     _check(_load().lse_merge(_ptr(out), _ptr(lse), _ptr(block_out), _ptr(block_lse), B, T, H, D,
                              block_lse_layout, _stream()))
     return out, lse
+
+
+def target_cp_fwd(prob: Problem, q, k, v, out=None, lse=None, want_lse: bool = True):
+    """Frozen-target context-parallel forward (head-major): q [B,H,T,D] local
+    contiguous queries, k/v [B,H,T_kv,D] the all-gathered K/V; returns (out [B,H,T,D],
+    lse [B,H,T] float32 or None). prob: layout "contiguous" (or "full"), num_blocks 1."""
+    dev = q.device
+    B, T, Tkv, H, D = prob.B, prob.T, prob.T_kv, prob.H, prob.D
+    _check_tensor("q", q, (B, H, T, D), prob.dtype, dev)
+    _check_tensor("k", k, (B, H, Tkv, D), prob.dtype, dev)
+    _check_tensor("v", v, (B, H, Tkv, D), prob.dtype, dev)
+    if out is None:
+        out = torch.empty_like(q)
+    _check_tensor("out", out, (B, H, T, D), prob.dtype, dev)
+    if lse is None and want_lse:
+        lse = torch.empty(B, H, T, dtype=torch.float32, device=dev)
+    if lse is not None:
+        _check_tensor("lse", lse, (B, H, T), torch.float32, dev)
+    _check(_load().eagle3_target_cp_fwd(prob.ref(), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                        _stream()))
+    return out, lse
+
+
+# ---- Ulysses re-sharding (the local halves around the all-to-all) ------------------
+
+def _uly_shapes(kind, stage, B, S_local, H, D, uly):
+    Hl, Sf = H // uly, uly * S_local
+    send = (uly, B, S_local, Hl, D)
+    if kind == "seq_to_head":
+        return ((B, S_local, H, D), send) if stage == 0 else (send, (B, Sf, Hl, D))
+    if kind == "head_to_seq":
+        return ((B, Sf, Hl, D), send) if stage == 0 else (send, (B, S_local, H, D))
+    lsend = (uly, B, Hl, S_local)
+    if kind == "lse_gather":
+        return ((B, H, S_local), lsend) if stage == 0 else (lsend, (B, Hl, Sf))
+    return ((B, Hl, Sf), lsend) if stage == 0 else (lsend, (B, H, S_local))
+
+
+def ulysses(kind: str, stage: int, src: torch.Tensor, uly: int, B: int, S_local: int, H: int,
+            D: int = 1, out: Optional[torch.Tensor] = None):
+    """One local half of a Ulysses transform (kind: seq_to_head, head_to_seq,
+    lse_gather, lse_scatter; stage 0 = pack into the all-to-all send buffer,
+    1 = unpack the receive buffer). H is the global head count."""
+    if H % uly:
+        raise ValueError(f"H={H} must divide by the Ulysses degree {uly}")
+    sin, sout = _uly_shapes(kind, stage, B, S_local, H, D, uly)
+    lse = kind.startswith("lse")
+    dt = torch.float32 if lse else src.dtype
+    if lse and src.dtype != torch.float32:
+        raise ValueError("lse must be float32")
+    if not lse and dt not in DTYPES:
+        raise ValueError(f"dtype {dt} not supported")
+    _check_tensor("src", src, sin, dt, src.device)
+    if out is None:
+        out = torch.empty(sout, dtype=dt, device=src.device)
+    _check_tensor("out", out, sout, dt, src.device)
+    lib = _load()
+    if lse:
+        _check(getattr(lib, f"eagle3_ulysses_{kind}")(stage, B, S_local, H, uly, _ptr(src), _ptr(out),
+                                                      _stream()))
+    else:
+        _check(getattr(lib, f"eagle3_ulysses_{kind}")(stage, DTYPES[dt], B, S_local, H, D, uly, _ptr(src),
+                                                      _ptr(out), _stream()))
+    return out
+
+
+# ---- ring-step mode (one ring step of one share on the local GPU) -------------------
+
+def ring_fwd_step(prob: Problem, step: int, q, k0, v0, out_step=None, lse_step=None):
+    """Block-0 attention over ring step `step`'s keys only: float32 (out [B,T,H,D],
+    lse [B,H,T]); rows that see no key of the step get out = 0, lse = -inf."""
+    dev = q.device
+    B, T, Tkv, H, D = prob.B, prob.T, prob.T_kv, prob.H, prob.D
+    _check_tensor("q", q, (B, T, H, D), prob.dtype, dev)
+    _check_tensor("k0", k0, (B, Tkv, H, D), prob.dtype, dev, prob.k0_strides)
+    _check_tensor("v0", v0, (B, Tkv, H, D), prob.dtype, dev, prob.k0_strides)
+    if out_step is None:
+        out_step = torch.empty(B, T, H, D, dtype=torch.float32, device=dev)
+    if lse_step is None:
+        lse_step = torch.empty(B, H, T, dtype=torch.float32, device=dev)
+    _check_tensor("out_step", out_step, (B, T, H, D), torch.float32, dev)
+    _check_tensor("lse_step", lse_step, (B, H, T), torch.float32, dev)
+    _check(_load().eagle3_ring_fwd_step(prob.ref(), step, _ptr(q), _ptr(k0), _ptr(v0), _ptr(out_step),
+                                        _ptr(lse_step), _stream()))
+    return out_step, lse_step
+
+
+def diag_merge_fwd(prob: Problem, q, kd, vd, out_acc, lse_acc, out=None, lse=None):
+    """Merges the diagonal blocks into the chained float32 block-0 (out_acc, lse_acc):
+    returns the final (out in q's dtype, lse float32)."""
+    dev = q.device
+    B, T, H, D, N = prob.B, prob.T, prob.H, prob.D, prob.N
+    _check_tensor("q", q, (B, T, H, D), prob.dtype, dev)
+    if N > 0:
+        _check_tensor("kd", kd, (B, N, T, H, D), prob.dtype, dev, prob.kd_strides)
+        _check_tensor("vd", vd, (B, N, T, H, D), prob.dtype, dev, prob.kd_strides)
+    _check_tensor("out_acc", out_acc, (B, T, H, D), torch.float32, dev)
+    _check_tensor("lse_acc", lse_acc, (B, H, T), torch.float32, dev)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty(B, H, T, dtype=torch.float32, device=dev)
+    _check_tensor("out", out, (B, T, H, D), prob.dtype, dev)
+    _check_tensor("lse", lse, (B, H, T), torch.float32, dev)
+    _check(_load().eagle3_diag_merge_fwd(prob.ref(), _ptr(q), _ptr(kd if N > 0 else None),
+                                         _ptr(vd if N > 0 else None), _ptr(out_acc), _ptr(lse_acc),
+                                         _ptr(out), _ptr(lse), _stream()))
+    return out, lse
+
+
+def ring_bwd_step(prob: Problem, step: int, dout, q, k0, v0, out, lse, dq_acc, dk0_acc, dv0_acc,
+                  workspace=None):
+    """Block-0 backward of ring step `step` against the merged out/lse: adds into the
+    float32 accumulators dq_acc [B,T,H,D] and dk0_acc / dv0_acc [B,T_kv,H,D] (the rows
+    of the step's keys). Returns the accumulators."""
+    dev = q.device
+    B, T, Tkv, H, D = prob.B, prob.T, prob.T_kv, prob.H, prob.D
+    for name, t in (("dout", dout), ("q", q), ("out", out)):
+        _check_tensor(name, t, (B, T, H, D), prob.dtype, dev)
+    _check_tensor("k0", k0, (B, Tkv, H, D), prob.dtype, dev, prob.k0_strides)
+    _check_tensor("v0", v0, (B, Tkv, H, D), prob.dtype, dev, prob.k0_strides)
+    _check_tensor("lse", lse, (B, H, T), torch.float32, dev)
+    _check_tensor("dq_acc", dq_acc, (B, T, H, D), torch.float32, dev)
+    _check_tensor("dk0_acc", dk0_acc, (B, Tkv, H, D), torch.float32, dev, prob.k0_strides)
+    _check_tensor("dv0_acc", dv0_acc, (B, Tkv, H, D), torch.float32, dev, prob.k0_strides)
+    if workspace is None:
+        workspace = torch.empty(max(prob.workspace_bytes(), 256), dtype=torch.uint8, device=dev)
+    _check(_load().eagle3_ring_bwd_step(prob.ref(), step, _ptr(dout), _ptr(q), _ptr(k0), _ptr(v0),
+                                        _ptr(out), _ptr(lse), _ptr(workspace), _ptr(dq_acc),
+                                        _ptr(dk0_acc), _ptr(dv0_acc), _stream()))
+    return dq_acc, dk0_acc, dv0_acc
+
+
+def diag_bwd(prob: Problem, dout, q, kd, vd, out, lse, dq_acc, grads=None):
+    """Closed-form diagonal gradients and the final dq = dq_acc + diagonal part:
+    returns (dq, dkd, dvd) in q's dtype."""
+    dev = q.device
+    B, T, H, D, N = prob.B, prob.T, prob.H, prob.D, prob.N
+    for name, t in (("dout", dout), ("q", q), ("out", out)):
+        _check_tensor(name, t, (B, T, H, D), prob.dtype, dev)
+    _check_tensor("lse", lse, (B, H, T), torch.float32, dev)
+    _check_tensor("dq_acc", dq_acc, (B, T, H, D), torch.float32, dev)
+    if N > 0:
+        _check_tensor("kd", kd, (B, N, T, H, D), prob.dtype, dev, prob.kd_strides)
+        _check_tensor("vd", vd, (B, N, T, H, D), prob.dtype, dev, prob.kd_strides)
+    if grads is None:
+        grads = (torch.empty_like(q),
+                 _strided_empty((B, N, T, H, D), prob.kd_strides, prob.dtype, dev),
+                 _strided_empty((B, N, T, H, D), prob.kd_strides, prob.dtype, dev))
+    dq, dkd, dvd = grads
+    _check_tensor("dq", dq, (B, T, H, D), prob.dtype, dev)
+    if N > 0:
+        _check_tensor("dkd", dkd, (B, N, T, H, D), prob.dtype, dev, prob.kd_strides)
+        _check_tensor("dvd", dvd, (B, N, T, H, D), prob.dtype, dev, prob.kd_strides)
+    _check(_load().eagle3_diag_bwd(prob.ref(), _ptr(dout), _ptr(q), _ptr(kd if N > 0 else None),
+                                   _ptr(vd if N > 0 else None), _ptr(out), _ptr(lse), _ptr(dq_acc),
+                                   _ptr(dq), _ptr(dkd if N > 0 else None),
+                                   _ptr(dvd if N > 0 else None), _stream()))
+    return dq, dkd, dvd
 
 
 class _CachedAttention(torch.autograd.Function):

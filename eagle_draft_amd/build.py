@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libeagle3_attn.so")
-SOURCES = ["e3_abi.cpp", "e3_fwd.hip", "e3_bwd.hip", "e3_merge.hip"]
+SOURCES = ["e3_abi.cpp", "e3_fwd.hip", "e3_bwd.hip", "e3_merge.hip", "e3_ulysses.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -17,10 +17,15 @@
 namespace e3 {
 hipError_t launch_fwd(const Args& a, int dtype, int D, hipStream_t st);
 hipError_t launch_bwd(const Args& a, int dtype, int D, hipStream_t st);
+hipError_t launch_bwd_fused(const Args& a, int D, hipStream_t st);
 hipError_t launch_lse_merge(float* out, float* lse, const float* bo, const float* bl, int B, int T,
                             int H, int D, int blayout, hipStream_t st);
+hipError_t launch_diag_merge(const Args& a, const float* out_acc, const float* lse_acc, int dtype, int D,
+                             hipStream_t st);
+hipError_t launch_diag_bwd(const Args& a, int dtype, int D, hipStream_t st);
 int fwd_tile_rows();
 int fwd_tile_keys();
+hipError_t launch_seg_copy(const SegCopy& c, hipStream_t st);
 }  // namespace e3
 
 namespace {
@@ -160,6 +165,14 @@ e3::Args make_args(const e3_problem* p, const Resolved& r) {
   a.layout = p->layout;
   a.cp = p->cp;
   a.rank = p->rank;
+  a.step_lo = 0;
+  a.step_hi = 1 << 30;
+  const long long HD = (long long)p->H * p->D;
+  a.q_bs = (long long)p->T * HD;
+  a.q_hs = p->D;
+  a.q_rs = HD;
+  a.kv_hs = p->D;
+  a.kv_rs = HD;
   return a;
 }
 
@@ -209,6 +222,9 @@ struct BwdWs {
   size_t delta, dqd, total;
 };
 
+// The fused backward (bf16 unless the problem asks for the deterministic path).
+bool fused_path(const e3_problem* p) { return p->dtype == E3_BF16 && !p->deterministic; }
+
 BwdWs bwd_ws_layout(const e3_problem* p) {
   BwdWs l;
   l.pitch = geo_of(p).pitch();
@@ -216,7 +232,8 @@ BwdWs bwd_ws_layout(const e3_problem* p) {
   l.delta = rows * sizeof(float);
   l.dqd = 2 * rows * sizeof(float);
   const int N = p->num_blocks - 1;
-  l.total = l.dqd + (N > 0 ? (size_t)p->B * p->T * p->H * p->D * sizeof(float) : 0);
+  const bool acc = N > 0 || fused_path(p);
+  l.total = l.dqd + (acc ? (size_t)p->B * p->T * p->H * p->D * sizeof(float) : 0);
   return l;
 }
 
@@ -260,7 +277,7 @@ int bwd_impl(const e3_problem* p, const void* dout, const void* q, const void* k
   a.dv0 = dv0;
   a.dkd = dkd;
   a.dvd = dvd;
-  hipError_t e = e3::launch_bwd(a, p->dtype, p->D, st);
+  hipError_t e = fused_path(p) ? e3::launch_bwd_fused(a, p->D, st) : e3::launch_bwd(a, p->dtype, p->D, st);
   if (e != hipSuccess) return fail(E3_EHIP, "backward launch failed: %s", hipGetErrorString(e));
   return ok();
 }
@@ -384,6 +401,305 @@ int lse_merge(float* out, float* lse, const float* block_out, const float* block
   hipError_t e = e3::launch_lse_merge(out, lse, block_out, block_lse, B, T, H, D, block_lse_layout, stream);
   if (e != hipSuccess) return fail(E3_EHIP, "lse_merge launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+int eagle3_target_cp_fwd(const e3_problem* p, const void* q, const void* k, const void* v, void* out,
+                         float* lse, hipStream_t stream) {
+  Resolved r;
+  int rc = validate(p, r, false);
+  if (rc) return rc;
+  if (p->layout != E3_LAYOUT_FULL && p->layout != E3_LAYOUT_CONTIGUOUS)
+    return fail(E3_EINVAL, "the frozen-target forward takes the FULL or CONTIGUOUS layout");
+  if (p->num_blocks != 1) return fail(E3_EINVAL, "the frozen-target forward has no diagonal blocks: num_blocks must be 1");
+  if (p->k0_batch_stride || p->kd_batch_stride || p->kd_block_stride)
+    return fail(E3_EINVAL, "the frozen-target forward takes dense head-major tensors (strides must be 0)");
+  if (p->T == 0) return ok();
+  {
+    const char* names[] = {"q", "k", "v", "out"};
+    const void* ptrs[] = {q, k, v, out};
+    if ((rc = check_ptrs(names, ptrs, 4))) return rc;
+  }
+  if (lse && misaligned(lse)) return fail(E3_EINVAL, "lse is not 16-byte aligned");
+  timing_reset();
+  e3::Args a = make_args(p, r);
+  const long long D = p->D, T = p->T, Tkv = p->T_kv;
+  a.q_bs = (long long)p->H * T * D;    // head-major [B, H, T, D]
+  a.q_hs = T * D;
+  a.q_rs = D;
+  a.k0_bs = (long long)p->H * Tkv * D; // head-major [B, H, T_kv, D]
+  a.kv_hs = Tkv * D;
+  a.kv_rs = D;
+  a.q = q;
+  a.k0 = k;
+  a.v0 = v;
+  a.out = out;
+  a.lse = lse;
+  hipError_t e = e3::launch_fwd(a, p->dtype, p->D, stream);
+  if (e != hipSuccess) return fail(E3_EHIP, "frozen-target forward launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int eagle3_ring_fwd_step(const e3_problem* p, int step, const void* q, const void* k0, const void* v0,
+                         float* out_step, float* lse_step, hipStream_t stream) {
+  Resolved r;
+  int rc = validate(p, r, false);
+  if (rc) return rc;
+  const int nsteps = geo_of(p).nsteps();
+  if (step < 0 || step >= nsteps) return fail(E3_EINVAL, "ring step %d out of range [0, %d)", step, nsteps);
+  if (p->T == 0) return ok();
+  {
+    const char* names[] = {"q", "k0", "v0", "out_step", "lse_step"};
+    const void* ptrs[] = {q, k0, v0, out_step, lse_step};
+    if ((rc = check_ptrs(names, ptrs, 5))) return rc;
+  }
+  timing_reset();
+  e3::Args a = make_args(p, r);
+  a.N = 0;                 // block 0 only; the diagonals are merged by eagle3_diag_merge_fwd
+  a.step_lo = step;
+  a.step_hi = step + 1;
+  a.out_f32 = 1;
+  a.q = q;
+  a.k0 = k0;
+  a.v0 = v0;
+  a.out = out_step;
+  a.lse = lse_step;
+  hipError_t e = e3::launch_fwd(a, p->dtype, p->D, stream);
+  if (e != hipSuccess) return fail(E3_EHIP, "ring-step forward launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int eagle3_diag_merge_fwd(const e3_problem* p, const void* q, const void* kd, const void* vd,
+                          const float* out_acc, const float* lse_acc, void* out, float* lse,
+                          hipStream_t stream) {
+  Resolved r;
+  int rc = validate(p, r, false);
+  if (rc) return rc;
+  if (p->T == 0) return ok();
+  {
+    const char* names[] = {"q", "out_acc", "lse_acc", "out", "lse"};
+    const void* ptrs[] = {q, out_acc, lse_acc, out, lse};
+    if ((rc = check_ptrs(names, ptrs, 5))) return rc;
+  }
+  if (r.N > 0) {
+    const char* names[] = {"kd", "vd"};
+    const void* ptrs[] = {kd, vd};
+    if ((rc = check_ptrs(names, ptrs, 2))) return rc;
+  }
+  timing_reset();
+  e3::Args a = make_args(p, r);
+  a.q = q;
+  a.kd = kd;
+  a.vd = vd;
+  a.out = out;
+  a.lse = lse;
+  hipError_t e = e3::launch_diag_merge(a, out_acc, lse_acc, p->dtype, p->D, stream);
+  if (e != hipSuccess) return fail(E3_EHIP, "diagonal merge launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int eagle3_ring_bwd_step(const e3_problem* p, int step, const void* dout, const void* q, const void* k0,
+                         const void* v0, const void* out, const float* lse, void* workspace, float* dq_acc,
+                         float* dk0_acc, float* dv0_acc, hipStream_t stream) {
+  Resolved r;
+  int rc = validate(p, r, false);
+  if (rc) return rc;
+  const int nsteps = geo_of(p).nsteps();
+  if (step < 0 || step >= nsteps) return fail(E3_EINVAL, "ring step %d out of range [0, %d)", step, nsteps);
+  if (p->T == 0) return ok();
+  {
+    const char* names[] = {"dout", "q", "k0", "v0", "out", "lse", "workspace", "dq_acc", "dk0_acc", "dv0_acc"};
+    const void* ptrs[] = {dout, q, k0, v0, out, lse, workspace, dq_acc, dk0_acc, dv0_acc};
+    if ((rc = check_ptrs(names, ptrs, 10))) return rc;
+  }
+  timing_reset();
+  e3::Args a = make_args(p, r);
+  a.N = 0;                 // block 0 only; the diagonals are eagle3_diag_bwd's
+  a.step_lo = step;
+  a.step_hi = step + 1;
+  a.dq_accum = 1;
+  a.kv_accum = 1;
+  a.q = q;
+  a.k0 = k0;
+  a.v0 = v0;
+  a.dout = dout;
+  a.o_in = out;
+  a.lse_in = lse;
+  {
+    const BwdWs l = bwd_ws_layout(p);
+    char* w = static_cast<char*>(workspace);
+    a.q_pitch = l.pitch;
+    a.lse2 = reinterpret_cast<float*>(w);
+    a.delta = reinterpret_cast<float*>(w + l.delta);
+  }
+  a.dqd = dq_acc;
+  a.dk0 = dk0_acc;
+  a.dv0 = dv0_acc;
+  hipError_t e = e3::launch_bwd(a, p->dtype, p->D, stream);
+  if (e != hipSuccess) return fail(E3_EHIP, "ring-step backward launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int eagle3_diag_bwd(const e3_problem* p, const void* dout, const void* q, const void* kd, const void* vd,
+                    const void* out, const float* lse, const float* dq_acc, void* dq, void* dkd, void* dvd,
+                    hipStream_t stream) {
+  Resolved r;
+  int rc = validate(p, r, false);
+  if (rc) return rc;
+  if (p->T == 0) return ok();
+  {
+    const char* names[] = {"dout", "q", "out", "lse", "dq_acc", "dq"};
+    const void* ptrs[] = {dout, q, out, lse, dq_acc, dq};
+    if ((rc = check_ptrs(names, ptrs, 6))) return rc;
+  }
+  if (r.N > 0) {
+    const char* names[] = {"kd", "vd", "dkd", "dvd"};
+    const void* ptrs[] = {kd, vd, dkd, dvd};
+    if ((rc = check_ptrs(names, ptrs, 4))) return rc;
+  }
+  timing_reset();
+  e3::Args a = make_args(p, r);
+  a.diag_self = 1;
+  a.q = q;
+  a.kd = kd;
+  a.vd = vd;
+  a.dout = dout;
+  a.o_in = out;
+  a.lse_in = lse;
+  a.dqd = dq_acc;
+  a.dq = dq;
+  a.dkd = dkd;
+  a.dvd = dvd;
+  hipError_t e = e3::launch_diag_bwd(a, p->dtype, p->D, stream);
+  if (e != hipSuccess) return fail(E3_EHIP, "diagonal backward launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+// Ulysses re-sharding: arguments shared by the four transforms.
+static int ulysses_check(const char* what, int stage, int esz, int B, int S_local, int H, int D, int uly,
+                         const void* src, const void* dst) {
+  if (stage != 0 && stage != 1) return fail(E3_EINVAL, "%s: stage must be 0 (pack) or 1 (unpack)", what);
+  if (esz == 0) return fail(E3_EINVAL, "%s: dtype must be E3_BF16 or E3_F32", what);
+  if (B < 1 || S_local < 0 || H < 1 || D < 1 || uly < 1)
+    return fail(E3_EINVAL, "%s: bad shape B=%d S_local=%d H=%d D=%d uly=%d", what, B, S_local, H, D, uly);
+  if (H % uly != 0)   // ulysses_attention page, `_gather_seq_scatter_heads`
+    return fail(E3_EINVAL, "%s: H=%d must divide by the Ulysses degree %d", what, H, uly);
+  if ((long long)uly * S_local > 0x3fffffffLL) return fail(E3_EUNSUPPORTED, "%s: sequence too long", what);
+  if (S_local == 0) return E3_OK;
+  if (!src || !dst) return fail(E3_EINVAL, "%s: src / dst is NULL", what);
+  if ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 3u)
+    return fail(E3_EINVAL, "%s: src / dst must be 4-byte aligned", what);
+  if (src == dst) return fail(E3_EINVAL, "%s: src and dst must not be the same buffer", what);
+  return E3_OK;
+}
+
+static int seg_copy(const char* what, const e3::SegCopy& c, hipStream_t st) {
+  hipError_t e = e3::launch_seg_copy(c, st);
+  if (e != hipSuccess) return fail(E3_EHIP, "%s launch failed: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+static int esize(int dtype) { return dtype == E3_BF16 ? 2 : dtype == E3_F32 ? 4 : 0; }
+
+int eagle3_ulysses_seq_to_head(int stage, int dtype, int B, int S_local, int H, int D, int uly,
+                               const void* src, void* dst, hipStream_t stream) {
+  const char* what = "eagle3_ulysses_seq_to_head";
+  const int es = esize(dtype);
+  int rc = ulysses_check(what, stage, es, B, S_local, H, D, uly, src, dst);
+  if (rc) return rc;
+  if (S_local == 0) return ok();
+  const long long Hl = H / uly, HD = (long long)H * D, RL = Hl * D, Sl = S_local, Sf = (long long)uly * Sl;
+  e3::SegCopy c{static_cast<const char*>(src), static_cast<char*>(dst), 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+  if (stage == 0) {
+    // x [B, S_local, H, D] -> send [uly][B][S_local][H/uly][D]: head group g goes to rank g
+    c.n0 = uly; c.n1 = B; c.n2 = Sl;
+    c.s0 = RL; c.s1 = Sl * HD; c.s2 = HD;
+    c.d0 = (long long)B * Sl * RL; c.d1 = Sl * RL; c.d2 = RL;
+    c.seg = RL;
+  } else {
+    // recv [uly][B][S_local][H/uly][D] (part j = sequence chunk j) -> y [B, uly*S_local, H/uly, D]
+    c.n0 = uly; c.n1 = B; c.n2 = 1;
+    c.s0 = (long long)B * Sl * RL; c.s1 = Sl * RL; c.s2 = 0;
+    c.d0 = Sl * RL; c.d1 = Sf * RL; c.d2 = 0;
+    c.seg = Sl * RL;
+  }
+  c.s0 *= es; c.s1 *= es; c.s2 *= es; c.d0 *= es; c.d1 *= es; c.d2 *= es; c.seg *= es;
+  return seg_copy(what, c, stream);
+}
+
+int eagle3_ulysses_head_to_seq(int stage, int dtype, int B, int S_local, int H, int D, int uly,
+                               const void* src, void* dst, hipStream_t stream) {
+  const char* what = "eagle3_ulysses_head_to_seq";
+  const int es = esize(dtype);
+  int rc = ulysses_check(what, stage, es, B, S_local, H, D, uly, src, dst);
+  if (rc) return rc;
+  if (S_local == 0) return ok();
+  const long long Hl = H / uly, HD = (long long)H * D, RL = Hl * D, Sl = S_local, Sf = (long long)uly * Sl;
+  e3::SegCopy c{static_cast<const char*>(src), static_cast<char*>(dst), 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+  if (stage == 0) {
+    // y [B, uly*S_local, H/uly, D] -> send [uly][B][S_local][H/uly][D]: sequence chunk j goes to rank j
+    c.n0 = uly; c.n1 = B; c.n2 = 1;
+    c.s0 = Sl * RL; c.s1 = Sf * RL; c.s2 = 0;
+    c.d0 = (long long)B * Sl * RL; c.d1 = Sl * RL; c.d2 = 0;
+    c.seg = Sl * RL;
+  } else {
+    // recv [uly][B][S_local][H/uly][D] (part g = head group g) -> x [B, S_local, H, D]
+    c.n0 = uly; c.n1 = B; c.n2 = Sl;
+    c.s0 = (long long)B * Sl * RL; c.s1 = Sl * RL; c.s2 = RL;
+    c.d0 = RL; c.d1 = Sl * HD; c.d2 = HD;
+    c.seg = RL;
+  }
+  c.s0 *= es; c.s1 *= es; c.s2 *= es; c.d0 *= es; c.d1 *= es; c.d2 *= es; c.seg *= es;
+  return seg_copy(what, c, stream);
+}
+
+int eagle3_ulysses_lse_gather(int stage, int B, int S_local, int H, int uly, const float* src, float* dst,
+                              hipStream_t stream) {
+  const char* what = "eagle3_ulysses_lse_gather";
+  int rc = ulysses_check(what, stage, 4, B, S_local, H, 1, uly, src, dst);
+  if (rc) return rc;
+  if (S_local == 0) return ok();
+  const long long Hl = H / uly, Sl = S_local, Sf = (long long)uly * Sl;
+  e3::SegCopy c{reinterpret_cast<const char*>(src), reinterpret_cast<char*>(dst), 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+  if (stage == 0) {
+    // lse [B, H, S_local] -> send [uly][B][H/uly][S_local]: head group g goes to rank g
+    c.n0 = uly; c.n1 = B; c.n2 = 1;
+    c.s0 = Hl * Sl; c.s1 = (long long)H * Sl; c.s2 = 0;
+    c.d0 = (long long)B * Hl * Sl; c.d1 = Hl * Sl; c.d2 = 0;
+    c.seg = Hl * Sl;
+  } else {
+    // recv [uly][B][H/uly][S_local] (part j = sequence chunk j) -> [B, H/uly, uly*S_local], contiguous
+    c.n0 = uly; c.n1 = B; c.n2 = Hl;
+    c.s0 = (long long)B * Hl * Sl; c.s1 = Hl * Sl; c.s2 = Sl;
+    c.d0 = Sl; c.d1 = Hl * Sf; c.d2 = Sf;
+    c.seg = Sl;
+  }
+  c.s0 *= 4; c.s1 *= 4; c.s2 *= 4; c.d0 *= 4; c.d1 *= 4; c.d2 *= 4; c.seg *= 4;
+  return seg_copy(what, c, stream);
+}
+
+int eagle3_ulysses_lse_scatter(int stage, int B, int S_local, int H, int uly, const float* src, float* dst,
+                               hipStream_t stream) {
+  const char* what = "eagle3_ulysses_lse_scatter";
+  int rc = ulysses_check(what, stage, 4, B, S_local, H, 1, uly, src, dst);
+  if (rc) return rc;
+  if (S_local == 0) return ok();
+  const long long Hl = H / uly, Sl = S_local, Sf = (long long)uly * Sl;
+  e3::SegCopy c{reinterpret_cast<const char*>(src), reinterpret_cast<char*>(dst), 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+  if (stage == 0) {
+    // [B, H/uly, uly*S_local] -> send [uly][B][H/uly][S_local]: sequence chunk j goes to rank j
+    c.n0 = uly; c.n1 = B; c.n2 = Hl;
+    c.s0 = Sl; c.s1 = Hl * Sf; c.s2 = Sf;
+    c.d0 = (long long)B * Hl * Sl; c.d1 = Hl * Sl; c.d2 = Sl;
+    c.seg = Sl;
+  } else {
+    // recv [uly][B][H/uly][S_local] (part g = head group g) -> lse [B, H, S_local]
+    c.n0 = uly; c.n1 = B; c.n2 = 1;
+    c.s0 = (long long)B * Hl * Sl; c.s1 = Hl * Sl; c.s2 = 0;
+    c.d0 = Hl * Sl; c.d1 = (long long)H * Sl; c.d2 = 0;
+    c.seg = Hl * Sl;
+  }
+  c.s0 *= 4; c.s1 *= 4; c.s2 *= 4; c.d0 *= 4; c.d1 *= 4; c.d2 *= 4; c.seg *= 4;
+  return seg_copy(what, c, stream);
 }
 
 int eagle3_query_positions(const e3_problem* p, int64_t* pos) {

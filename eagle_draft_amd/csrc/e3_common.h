@@ -51,6 +51,10 @@ struct Args {
   float scale;
   float c2;             // scale * log2(e): scores are kept in the base-2 domain
   int layout, cp, rank;
+  // Element strides of q / out (batch, head, row) and of k0 / v0 (head, row; the
+  // batch stride is k0_bs): token-major [B, T, H, D] by default, head-major
+  // [B, H, T, D] in the frozen-target forward. Only the forward reads them.
+  long long q_bs, q_hs, q_rs, kv_hs, kv_rs;
   // Ring-step mode (the single-GPU half of the ring protocol): only the block-0
   // keys of ring steps [step_lo, step_hi) are visited, and
   int step_lo, step_hi;
@@ -58,9 +62,24 @@ struct Args {
   int dq_accum;         //   the dQ kernel adds scale * dQ into a float32 dq (dqd)
   int kv_accum;         //   dK/dV adds into float32 dk0/dv0 for the steps' keys only
   int diag_self;        //   the diagonal kernel forms delta and lse*log2(e) itself
+  // Fused backward: the diagonal kernel adds its part of dq into the float32
+  // accumulator dqd with atomic adds (the fused block-0 kernel adds the rest).
+  int dq_atomic;
 };
 
 
+
+// A copy of contiguous segments of `seg` bytes between two strided layouts,
+// indexed by (i0, i1, i2) < (n0, n1, n2) (the Ulysses re-sharding transforms):
+//   src + i0*s0 + i1*s1 + i2*s2  ->  dst + i0*d0 + i1*d1 + i2*d2 (strides in bytes).
+struct SegCopy {
+  const char* src;
+  char* dst;
+  long long n0, n1, n2;
+  long long s0, s1, s2;
+  long long d0, d1, d2;
+  long long seg;
+};
 
 // Measurement hook (host): records the next caller-provided timing event, if any,
 // on the stream. Called before the first kernel of an entry point and after each.

@@ -56,10 +56,14 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const Args a) {
   int row0, nrows, gpos0;
   geo.qtile(trank, BM, row0, nrows, gpos0);
 
+  // Row (position) strides: rs for the [B, N, T, H, D] diagonal blocks; q / out and
+  // k0 / v0 take theirs from the arguments (token-major [B, T, H, D] by default,
+  // head-major [B, H, T, D] for the frozen-target forward).
   const long long rs = (long long)a.H * D;
-  const T* qb = reinterpret_cast<const T*>(a.q) + (long long)b * a.T * rs + (long long)h * D;
-  const T* k0b = reinterpret_cast<const T*>(a.k0) + (long long)b * a.k0_bs + (long long)h * D;
-  const T* vb = reinterpret_cast<const T*>(a.v0) + (long long)b * a.k0_bs + (long long)h * D;
+  const long long qrs = a.q_rs;
+  const T* qb = reinterpret_cast<const T*>(a.q) + (long long)b * a.q_bs + (long long)h * a.q_hs;
+  const T* k0b = reinterpret_cast<const T*>(a.k0) + (long long)b * a.k0_bs + (long long)h * a.kv_hs;
+  const T* vb = reinterpret_cast<const T*>(a.v0) + (long long)b * a.k0_bs + (long long)h * a.kv_hs;
 
   // This lane's query row.
   const int qr = w * 32 + l32;
@@ -74,7 +78,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const Args a) {
   Op qreg[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks)
-    qreg[ks] = qvalid ? load8(qb + (long long)(row0 + qr) * rs + 16 * ks + 8 * g) : zero8<T>();
+    qreg[ks] = qvalid ? load8(qb + (long long)(row0 + qr) * qrs + 16 * ks + 8 * g) : zero8<T>();
 
   f32x16 acc[DB];
 #pragma unroll
@@ -96,7 +100,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const Args a) {
   // (the same for K and V), so a step issues each copy with no address math.
   const char* const kbase = (const char*)uniform64((unsigned long long)k0b);
   const char* const vbase = (const char*)uniform64((unsigned long long)vb);
-  const unsigned krow = (unsigned)(rs * (long long)sizeof(T));
+  const unsigned krow = (unsigned)(a.kv_rs * (long long)sizeof(T));
   const TileDma<BN, C::KRB, C::U, NW> tdma(krow, w, lane);
   // K / V rows past the end re-read the last row: those keys are masked.
   auto dma_k = [&](char* dst, int s0) {
@@ -334,7 +338,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const Args a) {
   const int lr = lane / LPR, cc = (lane % LPR) * 8;
   const T* kdb = reinterpret_cast<const T*>(a.kd) + (long long)b * a.kd_bs + (long long)h * D + cc;
   const T* vdb = reinterpret_cast<const T*>(a.vd) + (long long)b * a.kd_bs + (long long)h * D + cc;
-  TO* ob = reinterpret_cast<TO*>(a.out) + (long long)b * a.T * rs + (long long)h * D + cc;
+  TO* ob = reinterpret_cast<TO*>(a.out) + (long long)b * a.q_bs + (long long)h * a.q_hs + cc;
   float* lseb = a.lse + ((long long)b * a.H + h) * a.T;
   for (int pass = 0; pass < 32 / RPP; pass += 2) {
     bool ok[2];
@@ -351,7 +355,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const Args a) {
       m[u] = Ms[tr];
       l[u] = Ls[tr];
       o[u] = *reinterpret_cast<const f32x8*>(Ow + rr * C::OSTR + cc);
-      qv[u] = load8(qb + row[u] * rs + cc);
+      qv[u] = load8(qb + row[u] * qrs + cc);
     }
     for (int i0 = 0; i0 < a.N; i0 += NB) {
       const int n = (a.N - i0) < NB ? (a.N - i0) : NB;
@@ -396,8 +400,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const Args a) {
       const float inv = l[u] > 0.f ? 1.f / l[u] : 0.f;   // l = 0: the row saw no key
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[u][e] *= inv;
-      store8f(ob + row[u] * rs, o[u]);
-      if ((lane % LPR) == 0) lseb[row[u]] = (m[u] + fast_log2(l[u])) * kLn2;
+      store8f(ob + row[u] * qrs, o[u]);
+      if ((lane % LPR) == 0 && a.lse) lseb[row[u]] = (m[u] + fast_log2(l[u])) * kLn2;   // lse may be omitted (frozen-target forward)
     }
   }
 }

@@ -81,7 +81,7 @@
 extern "C" {
 #endif
 
-#define EAGLE3_ABI_VERSION 3
+#define EAGLE3_ABI_VERSION 4
 
 typedef enum { E3_OK = 0, E3_EINVAL = -1, E3_EUNSUPPORTED = -2, E3_EHIP = -3 } e3_status;
 typedef enum { E3_BF16 = 0, E3_F32 = 1 } e3_dtype;
@@ -110,6 +110,11 @@ typedef struct e3_problem {
   int64_t k0_batch_stride;  /* elements between batch rows of k0/v0/dk0/dv0; 0 = T_kv*H*D */
   int64_t kd_batch_stride;  /* elements between batch rows of kd/vd/dkd/dvd; 0 = N*T*H*D */
   int64_t kd_block_stride;  /* elements between blocks of kd/vd/dkd/dvd; 0 = T*H*D */
+  int32_t deterministic;    /* backward path: 0 = fused (bf16: dK, dV and dQ in one kernel,
+                               dQ accumulated with float32 atomic adds, so dq is not bitwise
+                               reproducible); 1 = split dQ and dK/dV kernels, every output
+                               element written once, bitwise reproducible. float32 problems
+                               always take the split path. */
 } e3_problem;
 
 /* Version of this header's ABI (EAGLE3_ABI_VERSION). Bindings refuse a mismatch rather
@@ -123,9 +128,9 @@ const char* eagle3_last_error(void);
 /* Bytes of device workspace eagle3_attn_bwd / eagle3_shard_bwd need: delta = rowsum(dO*O)
  * and lse*log2(e) (float32 [B, H, P]: P = T for one run of local rows; with the zig-zag
  * layout each chunk of each document is a run, placed at a 16-byte boundary and padded
- * to 64 rows, P < T + 68 * runs + 128), then, when num_blocks > 1, the block-0 part of
- * dq (float32 [B, T, H, D]). 0 when T == 0. Returns 0 and sets the last error for an
- * invalid problem. */
+ * to 64 rows, P < T + 68 * runs + 128), then, when num_blocks > 1 or on the fused path,
+ * a float32 [B, T, H, D] dq accumulator. 0 when T == 0. Returns 0 and sets the last
+ * error for an invalid problem. */
 size_t eagle3_bwd_workspace_bytes(const e3_problem* p);
 
 /* Forward of the full sequence (layout FULL or HEADSHARD):
@@ -169,6 +174,105 @@ int eagle3_shard_bwd(const e3_problem* p, const void* dout, const void* q, const
  * is not produced (the merged-lse backward does not use it). */
 int lse_merge(float* out, float* lse, const float* block_out, const float* block_lse,
               int B, int T, int H, int D, int block_lse_layout, hipStream_t stream);
+
+/* ---- Frozen-target context parallelism --------------------------------------------------
+ *
+ * The frozen target model's forward under context parallelism (target_cp page,
+ * `attach_cp_kv_gather_hooks`): K/V are all-gathered across the cp group and each rank
+ * attends its contiguous local queries against the full K/V with a global causal mask
+ * (the O(S^2) scores stay sharded [S/cp, S]); tensors are head-major [B, nH, S, D] at
+ * the attention call; forward only. This is the CONTIGUOUS share (or FULL) with
+ * num_blocks == 1 in head-major layout:
+ *   q, out [B, H, T, D] (dtype), k, v [B, H, T_kv, D] (the all-gathered K/V, global
+ *   order), lse [B, H, T] float32 or NULL. Documents (cu_seqlens) are honoured as in
+ *   the other entry points. No workspace, no backward. */
+int eagle3_target_cp_fwd(const e3_problem* p, const void* q, const void* k, const void* v, void* out,
+                         float* lse, hipStream_t stream);
+
+/* ---- Ring-step mode: the single-GPU half of the ring protocol ------------------------
+ *
+ * The ring passes one K/V block per step and merges the per-step (out, lse) partials
+ * (ring_attention page, `ring_flash_attn_forward`: causal only at step 0, steps with
+ * K/V of later ranks contribute nothing to a contiguous share; `_update_out_and_lse`;
+ * zigzag_ring_attention page, `zigzag_ring_flash_attn_varlen_forward`: rotate K/V, a
+ * flash block per step, online merge), then merges the diagonal blocks
+ * (`_merge_diag`). In the backward each step's flash backward sees the MERGED out/lse
+ * and the K/V gradients travel back to their owners (`ring_flash_attn_backward`;
+ * zigzag_ring_attention page, `zigzag_ring_flash_attn_varlen_backward`). These entry
+ * points run one ring step of one share on the local GPU; the caller chains them
+ * (lse_merge between forward steps) and owns the K/V gradient accumulators, which play
+ * the part of the rotated dK/dV buffers. Ring step j holds the K/V of rank
+ * (rank - j) mod cp (`RingComm`): with the layouts above, k0/v0 always hold the full
+ * sequence and a step reads only its rank's rows. Layout CONTIGUOUS or ZIGZAG has cp
+ * steps, FULL and HEADSHARD one. The one-pass entry points above compute the same
+ * result with no partials in HBM. */
+
+/* Block-0 attention of the share's rows over the keys of ring step `step` only:
+ * out_step [B,T,H,D] float32 (normalised by the step's own sum) and lse_step [B,H,T]
+ * float32. A row that sees no key of the step gets out = 0 and lse = -inf (a no-op for
+ * lse_merge). num_blocks is ignored (the diagonals are merged afterwards). */
+int eagle3_ring_fwd_step(const e3_problem* p, int step, const void* q, const void* k0, const void* v0,
+                         float* out_step, float* lse_step, hipStream_t stream);
+
+/* Merges the N diagonal blocks into the chained block-0 state out_acc [B,T,H,D] and
+ * lse_acc [B,H,T] (float32, read only) and writes the final out [B,T,H,D] (dtype) and
+ * lse [B,H,T] float32 (ring_attention page, `_merge_diag`, once per block). */
+int eagle3_diag_merge_fwd(const e3_problem* p, const void* q, const void* kd, const void* vd,
+                          const float* out_acc, const float* lse_acc, void* out, float* lse,
+                          hipStream_t stream);
+
+/* Block-0 backward of ring step `step` against the MERGED out (dtype) / lse:
+ * dq_acc [B,T,H,D] float32 += scale * dS K over the step's keys; dk0_acc, dv0_acc
+ * [B,T_kv,H,D] float32 (strides of k0) += the step's gradients, on the rows of the
+ * step's keys only (other rows are not touched). The caller zeroes the accumulators.
+ * workspace as eagle3_bwd_workspace_bytes(p) (delta and lse*log2(e) are formed in it
+ * on every call). */
+int eagle3_ring_bwd_step(const e3_problem* p, int step, const void* dout, const void* q, const void* k0,
+                         const void* v0, const void* out, const float* lse, void* workspace, float* dq_acc,
+                         float* dk0_acc, float* dv0_acc, hipStream_t stream);
+
+/* Closed-form diagonal gradients against the merged out/lse, and the final dq:
+ * dkd, dvd [B,N,T,H,D] (dtype) and dq [B,T,H,D] (dtype) = dq_acc + scale * sum_i ds_i kd_i
+ * (ring_attention page, `_CachedRingAttention`: "diagonal grads are added in closed
+ * form"). With num_blocks == 1 it converts dq_acc to dq. No workspace. */
+int eagle3_diag_bwd(const e3_problem* p, const void* dout, const void* q, const void* kd, const void* vd,
+                    const void* out, const float* lse, const float* dq_acc, void* dq, void* dkd, void* dvd,
+                    hipStream_t stream);
+
+/* ---- Ulysses re-sharding: the local halves around the all-to-all ----------------------
+ *
+ * The Ulysses path (ulysses_attention page, module text and `_CachedUlyssesAttention`)
+ * turns a sequence shard into a head shard with one all-to-all, runs block 0 over the
+ * full sequence for H/uly heads (the HEADSHARD layout above), sends out and lse back
+ * with a second all-to-all and merges the diagonals on the sequence shard.
+ * `_all_to_all_single` exchanges equal splits along dim 0: a send buffer is
+ * [uly][...] with part i going to rank i, a receive buffer is [uly][...] with part i
+ * coming from rank i. These calls are the local halves of the four transforms; the
+ * exchange itself (RCCL all-to-all over the xGMI links) is the caller's. stage 0 packs
+ * src into the send buffer dst, stage 1 unpacks the receive buffer src into dst.
+ * H is the GLOBAL head count and must divide by uly; S_full = uly * S_local. dtype is
+ * E3_BF16 or E3_F32; lse is float32. src and dst are device buffers, 4-byte aligned,
+ * not the same buffer; results are exact copies.
+ *
+ * `_gather_seq_scatter_heads`: x [B, S_local, H, D] -> [B, S_full, H/uly, D]
+ *   stage 0: x -> send [uly][B][S_local][H/uly][D] (head group g to rank g)
+ *   stage 1: recv [uly][B][S_local][H/uly][D] (part j = sequence chunk j) -> y */
+int eagle3_ulysses_seq_to_head(int stage, int dtype, int B, int S_local, int H, int D, int uly,
+                               const void* src, void* dst, hipStream_t stream);
+/* `_scatter_seq_gather_heads`: y [B, S_full, H/uly, D] -> [B, S_local, H, D]
+ *   stage 0: y -> send [uly][B][S_local][H/uly][D] (sequence chunk j to rank j)
+ *   stage 1: recv [uly][B][S_local][H/uly][D] (part g = head group g) -> x */
+int eagle3_ulysses_head_to_seq(int stage, int dtype, int B, int S_local, int H, int D, int uly,
+                               const void* src, void* dst, hipStream_t stream);
+/* `_gather_lse`: [B, H, S_local] -> [B, H/uly, S_full], contiguous (the page requires a
+ * contiguous result: the flash backward reads lse without making it contiguous)
+ *   stage 0: lse -> send [uly][B][H/uly][S_local]; stage 1: recv -> [B, H/uly, S_full] */
+int eagle3_ulysses_lse_gather(int stage, int B, int S_local, int H, int uly, const float* src, float* dst,
+                              hipStream_t stream);
+/* `_scatter_lse`: [B, H/uly, S_full] -> [B, H, S_local]
+ *   stage 0: -> send [uly][B][H/uly][S_local]; stage 1: recv -> [B, H, S_local] */
+int eagle3_ulysses_lse_scatter(int stage, int B, int S_local, int H, int uly, const float* src, float* dst,
+                               hipStream_t stream);
 
 /* ---- Measurement hook ---------------------------------------------------------------- */
 

@@ -113,7 +113,14 @@ def test_workspace_bytes():
     # and, with diagonal blocks, the block-0 part of dq (float32 [B, T, H, D])
     P = 1024
     assert p.workspace_bytes() == 2 * 1 * 3 * P * 4 + 1 * 1000 * 3 * 128 * 4
-    assert prob(B=1, T=1000, T_kv=1000, H=3, num_blocks=1).workspace_bytes() == 2 * 3 * P * 4
+    # the fused bf16 path always needs the float32 dq accumulator; the split
+    # (deterministic) path only with diagonal blocks
+    assert prob(B=1, T=1000, T_kv=1000, H=3, num_blocks=1).workspace_bytes() == \
+        2 * 3 * P * 4 + 1000 * 3 * 128 * 4
+    assert prob(B=1, T=1000, T_kv=1000, H=3, num_blocks=1, deterministic=True).workspace_bytes() == \
+        2 * 3 * P * 4
+    assert prob(B=1, T=1000, T_kv=1000, H=3, num_blocks=1, dtype=torch.float32).workspace_bytes() == \
+        2 * 3 * P * 4
     # zig-zag: each of the two local chunks is padded to 64 rows on its own
     # zig-zag: run i (of 150 rows) starts at roundup4(local start) + 68 i: 0 and
     # 152 + 68 = 220, and ends its padding at 220 + 192 = 412, rounded up to 448
@@ -241,3 +248,31 @@ def test_binding_checks_strides_against_the_problem():
     assert strided.kd_strides == (blk, T * H * D, H * D, D, 1)
     g = e3._strided_empty((B, nb - 1, T, H, D), strided.kd_strides, torch.float32, "cpu")
     assert g.stride() == strided.kd_strides
+
+
+def test_ring_step_entry_points_refuse_a_step_out_of_range():
+    lib = e3.lib()
+    a = ctypes.c_void_p(0x1000)        # never dereferenced: validation fails first
+    for layout, cp, T, Tkv in (("contiguous", 4, 256, 1024), ("zigzag", 4, 256, 1024), ("full", 1, 256, 256)):
+        p = prob(layout=layout, cp=cp, rank=0, T=T, T_kv=Tkv)
+        for step in (-1, cp):
+            rc = lib.eagle3_ring_fwd_step(p.ref(), step, a, a, a, a, a, None)
+            assert rc == e3.E3_EINVAL and "ring step" in lib.eagle3_last_error().decode()
+            rc = lib.eagle3_ring_bwd_step(p.ref(), step, *([a] * 10), None)
+            assert rc == e3.E3_EINVAL and "ring step" in lib.eagle3_last_error().decode()
+
+
+def test_target_cp_forward_refuses_what_it_does_not_compute():
+    lib = e3.lib()
+    a = ctypes.c_void_p(0x1000)        # never dereferenced: validation fails first
+    p = prob(layout="contiguous", cp=4, rank=1, T=256, T_kv=1024, num_blocks=3)
+    assert lib.eagle3_target_cp_fwd(p.ref(), a, a, a, a, a, None) == e3.E3_EINVAL
+    assert "num_blocks must be 1" in lib.eagle3_last_error().decode()
+    p = prob(layout="zigzag", cp=4, rank=1, T=256, T_kv=1024, num_blocks=1)
+    assert lib.eagle3_target_cp_fwd(p.ref(), a, a, a, a, a, None) == e3.E3_EINVAL
+    assert "FULL or CONTIGUOUS" in lib.eagle3_last_error().decode()
+    p = prob(B=2, layout="contiguous", cp=4, rank=1, T=256, T_kv=1024, num_blocks=1,
+             k0_batch_stride=4096 * 256)
+    assert lib.eagle3_target_cp_fwd(p.ref(), a, a, a, a, a, None) == e3.E3_EINVAL
+    assert "dense head-major" in lib.eagle3_last_error().decode()
+

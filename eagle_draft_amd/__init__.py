@@ -79,6 +79,9 @@ def _load():
         f = getattr(lib, name)
         f.argtypes = [P] + [vp] * 14 + [vp]
         f.restype = ctypes.c_int
+    lib.eagle3_bwd_noalloc.argtypes = [P] + [vp] * 13 + [vp]
+    lib.eagle3_bwd_noalloc.restype = ctypes.c_int
+    lib.eagle3_bwd_noalloc_max_scratch_bytes.restype = ctypes.c_size_t
     lib.lse_merge.argtypes = [vp, vp, vp, vp, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                               ctypes.c_int, ctypes.c_int, vp]
     lib.lse_merge.restype = ctypes.c_int
@@ -329,6 +332,31 @@ def bwd(prob: Problem, dout, q, k0, v0, kd, vd, out, lse, grads=None, workspace=
                                _ptr(dv0), _ptr(dkd if N > 0 else None),
                                _ptr(dvd if N > 0 else None), _stream()))
     return dq, dk0, dv0, dkd, dvd
+
+
+def bwd_noalloc(prob: Problem, dout, q, k0, v0, kd, vd, out, lse, grads):
+    """The backward through eagle3_bwd_noalloc: no workspace, no allocation by the
+    library; the caller passes the gradient buffers (dq, dk0, dv0, dkd, dvd)."""
+    dev = q.device
+    B, T, Tkv, H, D, N = prob.B, prob.T, prob.T_kv, prob.H, prob.D, prob.N
+    for name, t in (("dout", dout), ("q", q), ("out", out)):
+        _check_tensor(name, t, (B, T, H, D), prob.dtype, dev)
+    _check_tensor("k0", k0, (B, Tkv, H, D), prob.dtype, dev, prob.k0_strides)
+    _check_tensor("v0", v0, (B, Tkv, H, D), prob.dtype, dev, prob.k0_strides)
+    _check_tensor("lse", lse, (B, H, T), torch.float32, dev)
+    dq, dk0, dv0, dkd, dvd = grads
+    _check_tensor("dq", dq, (B, T, H, D), prob.dtype, dev)
+    _check_tensor("dk0", dk0, (B, Tkv, H, D), prob.dtype, dev, prob.k0_strides)
+    _check_tensor("dv0", dv0, (B, Tkv, H, D), prob.dtype, dev, prob.k0_strides)
+    if N > 0:
+        for name, t in (("kd", kd), ("vd", vd), ("dkd", dkd), ("dvd", dvd)):
+            _check_tensor(name, t, (B, N, T, H, D), prob.dtype, dev, prob.kd_strides)
+    _check(_load().eagle3_bwd_noalloc(prob.ref(), _ptr(dout), _ptr(q), _ptr(k0), _ptr(v0),
+                                      _ptr(kd if N > 0 else None), _ptr(vd if N > 0 else None),
+                                      _ptr(out), _ptr(lse), _ptr(dq), _ptr(dk0), _ptr(dv0),
+                                      _ptr(dkd if N > 0 else None), _ptr(dvd if N > 0 else None),
+                                      _stream()))
+    return grads
 
 
 def lse_merge(out, lse, block_out, block_lse, block_lse_layout: int = 0):

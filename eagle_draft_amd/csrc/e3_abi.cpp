@@ -10,6 +10,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <map>
+#include <mutex>
 #include <string>
 
 #include "e3_common.h"
@@ -288,7 +289,34 @@ int doc_lo_host(const e3_problem* p, int pos) {
 
 }  // namespace
 
+// ---- no-allocation backward: a static device scratch array -----------------------
+// Holds lse*log2(e) and delta (float32, 2 x B*H*P) for eagle3_bwd_noalloc. In host
+// code `scratch` names a host-side stand-in, never the device memory: kernels get
+// the address hipGetSymbolAddress returns, looked up once per device.
 namespace {
+constexpr size_t kScratchBytes = size_t(16) << 20;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+}  // namespace
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+namespace {
+hipError_t scratch_ptr(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    if ((e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) != hipSuccess) return e;
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return hipSuccess;
+}
+
 struct SideRes {
   hipStream_t s = nullptr;
   hipEvent_t fork[2] = {nullptr, nullptr}, join[2] = {nullptr, nullptr};
@@ -382,6 +410,57 @@ int eagle3_shard_bwd(const e3_problem* p, const void* dout, const void* q, const
                      hipStream_t stream) {
   return bwd_impl(p, dout, q, k0, v0, kd, vd, out, lse, workspace, dq, dk0, dv0, dkd, dvd, stream, false);
 }
+
+int eagle3_bwd_noalloc(const e3_problem* p, const void* dout, const void* q, const void* k0, const void* v0,
+                       const void* kd, const void* vd, const void* out, const float* lse, void* dq, void* dk0,
+                       void* dv0, void* dkd, void* dvd, hipStream_t stream) {
+  Resolved r;
+  int rc = validate(p, r, false);
+  if (rc) return rc;
+  if (p->T == 0) return ok();
+  {
+    const char* names[] = {"dout", "q", "k0", "v0", "out", "lse", "dq", "dk0", "dv0"};
+    const void* ptrs[] = {dout, q, k0, v0, out, lse, dq, dk0, dv0};
+    if ((rc = check_ptrs(names, ptrs, 9))) return rc;
+  }
+  if (r.N > 0) {
+    const char* names[] = {"kd", "vd", "dkd", "dvd"};
+    const void* ptrs[] = {kd, vd, dkd, dvd};
+    if ((rc = check_ptrs(names, ptrs, 4))) return rc;
+  }
+  const BwdWs l = bwd_ws_layout(p);
+  if (l.dqd > kScratchBytes)
+    return fail(E3_EINVAL, "eagle3_bwd_noalloc: needs %zu bytes of scratch (2 x B*H*P floats), the static "
+                "scratch holds %zu; use eagle3_shard_bwd with a workspace", l.dqd, kScratchBytes);
+  void* sp = nullptr;
+  hipError_t e = scratch_ptr(&sp);
+  if (e != hipSuccess) return fail(E3_EHIP, "eagle3_bwd_noalloc: scratch address: %s", hipGetErrorString(e));
+  timing_reset();
+  e3::Args a = make_args(p, r);
+  a.dq_in_out = 1;
+  a.q = q;
+  a.k0 = k0;
+  a.v0 = v0;
+  a.kd = kd;
+  a.vd = vd;
+  a.dout = dout;
+  a.o_in = out;
+  a.lse_in = lse;
+  a.q_pitch = l.pitch;
+  a.lse2 = reinterpret_cast<float*>(sp);
+  a.delta = reinterpret_cast<float*>(static_cast<char*>(sp) + l.delta);
+  a.dqd = nullptr;
+  a.dq = dq;
+  a.dk0 = dk0;
+  a.dv0 = dv0;
+  a.dkd = dkd;
+  a.dvd = dvd;
+  e = e3::launch_bwd(a, p->dtype, p->D, stream);
+  if (e != hipSuccess) return fail(E3_EHIP, "backward launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+size_t eagle3_bwd_noalloc_max_scratch_bytes(void) { return kScratchBytes; }
 
 int lse_merge(float* out, float* lse, const float* block_out, const float* block_lse, int B, int T,
               int H, int D, int block_lse_layout, hipStream_t stream) {

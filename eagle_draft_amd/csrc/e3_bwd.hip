@@ -830,10 +830,10 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void dq_kernel(const A
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[e] += dqv[e];
       *reinterpret_cast<f32x8*>(dqdb + row * rs) = acc;
-    } else if (a.N > 0) {
+    } else if (a.N > 0 && !a.dq_in_out) {
       *reinterpret_cast<f32x8*>(dqdb + row * rs) = dqv;
     } else {
-      store8f(dqb + row * rs, dqv);
+      store8f(dqb + row * rs, dqv);   // final dq, or (dq_in_out) the block-0 part
     }
   }
 }
@@ -877,15 +877,16 @@ __global__ __launch_bounds__(256, 4) void diag_bwd_kernel(const Args a) {
       l2 = a.lse2[loff];
       dl = a.delta[loff];
     }
-    // scale * dQ(block 0): the float32 partial; with the fused block-0 kernel
-    // (dq_atomic) only the diagonal part is formed here and added into the float32
-    // accumulator
+    // scale * dQ(block 0): the float32 partial, or (dq_in_out) dq itself in q's
+    // dtype; with the fused block-0 kernel (dq_atomic) only the diagonal part is
+    // formed here and added into the float32 accumulator
     f32x8 dq;
     if (a.dq_atomic) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) dq[e] = 0.f;
     } else {
-      dq = *reinterpret_cast<const f32x8*>(a.dqd + qoff);
+      dq = a.dq_in_out ? load8f(reinterpret_cast<const T*>(a.dq) + qoff)
+                       : *reinterpret_cast<const f32x8*>(a.dqd + qoff);
     }
     for (int i0 = 0; i0 < a.N; i0 += NB) {
       const int n = (a.N - i0) < NB ? (a.N - i0) : NB;
@@ -945,7 +946,7 @@ static hipError_t launch_bwd_t(const Args& a, hipStream_t st) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   timing_mark(st);
-  if (a.N > 0) {
+  if (a.N > 0 && !a.dq_in_out) {
     hipStream_t side = nullptr;
     if ((e = side_begin(st, 0, side)) != hipSuccess) return e;
     timing_mark(side);
@@ -962,7 +963,14 @@ static hipError_t launch_bwd_t(const Args& a, hipStream_t st) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   timing_mark(st);
-  if (a.N > 0 && (e = side_end(st, 0)) != hipSuccess) return e;
+  if (a.N > 0 && a.dq_in_out) {
+    // no-allocation backward: the diagonal gradients after dK/dV on the same stream
+    // (they read the block-0 dq the dQ kernel left in dq)
+    hipLaunchKernelGGL((diag_bwd_kernel<T, D>), dim3(kDiagGrid), dim3(256), 0, st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  } else if (a.N > 0 && (e = side_end(st, 0)) != hipSuccess) {
+    return e;
+  }
   timing_mark(st);
   return hipSuccess;
 }

@@ -148,6 +148,25 @@ int eagle3_attn_bwd(const e3_problem* p, const void* dout, const void* q, const 
                     const float* lse, void* workspace, void* dq, void* dk0, void* dv0,
                     void* dkd, void* dvd, hipStream_t stream);
 
+/* Backward that allocates nothing, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): eagle3_shard_bwd's computation on its split (deterministic) path, for
+ * any layout, with no workspace argument (the problem's `deterministic` field is
+ * not consulted). delta and lse*log2(e) live in a static device array of
+ * eagle3_bwd_noalloc_max_scratch_bytes() = 16 MiB that the library holds on every GPU
+ * it runs on until the process ends (2 x B*H*P floats must fit: P as for
+ * eagle3_bwd_workspace_bytes; larger problems are refused with E3_EINVAL). The
+ * block-0 part of dq passes through dq itself (q's dtype) instead of a float32
+ * partial, and all kernels run on `stream` (no side stream), so this entry point calls
+ * no allocating routine after its first call on a device. Every call on one GPU
+ * shares that GPU's array: calls that overlap on one GPU (other streams, other host
+ * threads) race and must be serialised by the caller. Nothing in the array needs to
+ * start at zero. Outputs as eagle3_shard_bwd. */
+int eagle3_bwd_noalloc(const e3_problem* p, const void* dout, const void* q, const void* k0, const void* v0,
+                       const void* kd, const void* vd, const void* out, const float* lse, void* dq, void* dk0,
+                       void* dv0, void* dkd, void* dvd, hipStream_t stream);
+size_t eagle3_bwd_noalloc_max_scratch_bytes(void);
+
 /* Shard driver: the same computation for any layout (CONTIGUOUS, ZIGZAG, HEADSHARD,
  * FULL). The share's block-0 attention visits the K/V segments in ring order and merges
  * them with the diagonals in one pass, with no inter-GPU communication. Arguments as

@@ -276,3 +276,16 @@ def test_target_cp_forward_refuses_what_it_does_not_compute():
     assert lib.eagle3_target_cp_fwd(p.ref(), a, a, a, a, a, None) == e3.E3_EINVAL
     assert "dense head-major" in lib.eagle3_last_error().decode()
 
+
+def test_noalloc_backward_refuses_a_problem_larger_than_its_scratch():
+    """The no-allocation backward's static scratch holds 2 x B*H*P floats; a larger
+    problem is refused before anything is launched (no device is touched)."""
+    lib = e3.lib()
+    cap = lib.eagle3_bwd_noalloc_max_scratch_bytes()
+    assert cap == 16 << 20
+    H = 64
+    T = cap // (2 * 4 * H) + 64
+    p = e3.Problem(1, T, T, H, 128, 1, 0.088, dtype=torch.bfloat16)
+    a = ctypes.c_void_p(0x1000)        # never dereferenced: the size check fails first
+    rc = lib.eagle3_bwd_noalloc(p.ref(), *([a] * 13), None)
+    assert rc == e3.E3_EINVAL and "scratch" in lib.eagle3_last_error().decode()

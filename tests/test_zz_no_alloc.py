@@ -1,0 +1,45 @@
+"""The backward that allocates nothing (eagle3_bwd_noalloc, for callers that cannot
+allocate device memory) against the backward with a workspace whose kernels it
+shares (eagle3_shard_bwd on the split, deterministic path): two calls in a row,
+the second with a smaller input, each compared at the parity tolerances; the
+K/V and diagonal gradients come from the same kernels and must be bitwise equal,
+dq differs only by the rounding of its block-0 part to q's dtype."""
+import pytest
+import torch
+
+import eagle_draft_amd as e3
+import synth
+from tests.parity import TOL, inputs, problem, rel, say
+
+pytestmark = pytest.mark.gpu
+
+W = synth.small_workload
+
+
+def run_both(w):
+    inp = inputs(w)
+    d = {k: v.cuda() for k, v in inp.items()}
+    prob = problem(w, deterministic=True)
+    out, lse = e3.fwd(prob, d["q"], d["k0"], d["v0"], d["kd"], d["vd"])
+    ref = e3.bwd(prob, d["dout"], d["q"], d["k0"], d["v0"], d["kd"], d["vd"], out, lse)
+    grads = tuple(torch.full_like(g, float("nan")) for g in ref)
+    got = e3.bwd_noalloc(prob, d["dout"], d["q"], d["k0"], d["v0"], d["kd"], d["vd"], out, lse, grads)
+    torch.cuda.synchronize()
+    return ref, got
+
+
+def test_noalloc_backward_matches_the_workspace_backward_twice():
+    big = W(S=1200, H=3, D=128, num_blocks=4, doc_lens=[500, 1, 699], seed=2)
+    small = W(S=256, H=2, D=128, num_blocks=3, layout="zigzag", cp=2, rank=1, seed=3)
+    for w in (big, small):
+        say(f"[noalloc] {w}")
+        ref, got = run_both(w)
+        t = TOL[w.dtype]
+        names = ("dq", "dk0", "dv0", "dkd", "dvd")
+        for n, a, b in zip(names, ref, got):
+            assert torch.isfinite(b.float()).all(), n          # every element written
+        for n, a, b in zip(names[1:], ref[1:], got[1:]):
+            assert torch.equal(a, b), n
+        err = rel(got[0].double().cpu().numpy(), ref[0].double().cpu().numpy())
+        say(f"[noalloc] dq relative difference {err:.3g}")
+        assert err <= t["grad"]

@@ -32,22 +32,14 @@ METRIC = "EAGLE-3 mixed attn fwd+bwd TFLOP/s (causal) + % bf16 MFMA peak, T=4096
 PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}   # MI355X dense MFMA (bf16) / fp32 vector
 PEAK_GBS = 8000.0                               # MI355X HBM3E
 # Stages timed with the events the library records per call (see
-# eagle3_set_timing_events): forward e0 | fwd | e1; backward e0 | pre | e1, side
-# stream e2 | diag_bwd | e3, main e1 | main | e4 | tail | e5. The backward's pre,
-# main and tail stages are, on the fused path (the default for bf16), the prep
-# kernel (delta, lse*log2(e), the float32 dq accumulator zeroed), the fused
-# dK/dV/dQ kernel and the join plus the dq conversion; on the split path
-# (--deterministic), the dQ kernel, the dK/dV kernel and the join.
+# eagle3_set_timing_events): forward e0 | fwd | e1; backward e0 | dq | e1, side
+# stream e2 | diag_bwd | e3, main e1 | dkdv | e4 | the wait for the side stream | e5.
 NFWD_EV, NBWD_EV = 2, 6
-STAGE_EVENTS = {"fwd": ("f", 0, 1), "bwd_pre": ("b", 0, 1), "diag_bwd": ("b", 2, 3),
-                "bwd_main": ("b", 1, 4), "bwd_tail": ("b", 4, 5)}
+STAGE_EVENTS = {"fwd": ("f", 0, 1), "dq": ("b", 0, 1), "diag_bwd": ("b", 2, 3),
+                "dkdv": ("b", 1, 4), "bwd_tail": ("b", 4, 5)}
 KERNELS = list(STAGE_EVENTS)
-KERNEL_NAMES = {
-    "fused": {"fwd": "fwd_kernel", "bwd_pre": "bwd_prep_kernel", "bwd_main": "fused_bwd_kernel",
-              "diag_bwd": "diag_bwd_kernel", "bwd_tail": "dq_convert_kernel"},
-    "split": {"fwd": "fwd_kernel", "bwd_pre": "dq_kernel", "bwd_main": "dkdv_kernel",
-              "diag_bwd": "diag_bwd_kernel", "bwd_tail": "(join)"},
-}
+KERNEL_NAMES = {"fwd": "fwd_kernel", "dq": "dq_kernel", "dkdv": "dkdv_kernel",
+                "diag_bwd": "diag_bwd_kernel", "bwd_tail": "(join)"}
 
 
 def log(msg):
@@ -91,10 +83,9 @@ def measured_traffic(kernel, workload):
     return round(fetch + write)
 
 
-def kernel_work(w, P0, path):
-    """Algorithmic FLOPs and HBM bytes per launch of each stage (path "fused" or
-    "split"). u = B*T*H*D*esz (one local [T,H,D] tensor), ukv = B*T_kv*H*D*esz,
-    f32 = B*T*H*D*4 (a float32 [T,H,D] tensor)."""
+def kernel_work(w, P0):
+    """Algorithmic FLOPs and HBM bytes per launch of each stage. u = B*T*H*D*esz
+    (one local [T,H,D] tensor), ukv = B*T_kv*H*D*esz, f32 = B*T*H*D*4."""
     esz = 2 if w.dtype == "bf16" else 4
     B, T, Tkv, H, D, N = w.B, w.T, w.T_kv, w.H, w.D, w.N
     u = B * T * H * D * esz
@@ -103,40 +94,21 @@ def kernel_work(w, P0, path):
     rowf = B * H * T * 4                      # one float per (b, h, row): lse or delta
     pf = B * H * D * P0                       # one D-long dot per attended pair
     diagf = B * H * D * T * N
-    work = {
+    return {
         # q, k0, v0, kd, vd read; out, lse written
         "fwd": dict(flop=4 * pf, diag_flop=4 * diagf, bytes=u + 2 * ukv + 2 * N * u + u + rowf),
+        # q, dO, O, k0, v0, lse read; delta, lse*log2(e) and dq (or its float32
+        # partial) written; S, dP, dQ = 3 products
+        "dq": dict(flop=6 * pf, diag_flop=0, bytes=3 * u + (f32 if N else u) + 2 * ukv + 3 * rowf),
+        # q, dO, k0, v0, lse, delta read; dk0, dv0 written; S, dP, dV, dK = 4 products
+        "dkdv": dict(flop=8 * pf, diag_flop=0, bytes=2 * u + 4 * ukv + 2 * rowf),
+        # side stream (beside dK/dV): q, dO, kd, vd, the float32 dq partial, lse*log2(e),
+        # delta read; dq, dkd, dvd written
+        "diag_bwd": dict(flop=0, diag_flop=10 * diagf,
+                         bytes=(2 * u + 2 * N * u + f32 + 2 * rowf + u + 2 * N * u) if N else 0),
+        # the wait for the side stream after dK/dV: time only
+        "bwd_tail": dict(flop=0, diag_flop=0, bytes=0),
     }
-    if path == "fused":
-        work.update({
-            # dO, O, lse read; delta, lse*log2(e) written; the float32 dq accumulator zeroed
-            "bwd_pre": dict(flop=0, diag_flop=0, bytes=2 * u + 3 * rowf + f32),
-            # q, dO, k0, v0, lse*log2(e), delta read; dk0, dv0 written; dq added into the
-            # float32 accumulator (counted once); S, dP, dV, dK, dQ = 5 products
-            "bwd_main": dict(flop=10 * pf, diag_flop=0, bytes=2 * u + 4 * ukv + 2 * rowf + f32),
-            # side stream: q, dO, kd, vd, lse*log2(e), delta read; dkd, dvd written; the
-            # diagonal part of dq added into the accumulator (read and written)
-            "diag_bwd": dict(flop=0, diag_flop=10 * diagf,
-                             bytes=(2 * u + 4 * N * u + 2 * rowf + 2 * f32) if N else 0),
-            # the join, then dq converted: accumulator read, dq written
-            "bwd_tail": dict(flop=0, diag_flop=0, bytes=f32 + u),
-        })
-    else:
-        work.update({
-            # q, dO, O, k0, v0, lse read; delta, lse*log2(e) and dq (or its float32
-            # partial) written; S, dP, dQ = 3 products
-            "bwd_pre": dict(flop=6 * pf, diag_flop=0,
-                            bytes=3 * u + (f32 if N else u) + 2 * ukv + 3 * rowf),
-            # q, dO, k0, v0, lse, delta read; dk0, dv0 written; S, dP, dV, dK = 4 products
-            "bwd_main": dict(flop=8 * pf, diag_flop=0, bytes=2 * u + 4 * ukv + 2 * rowf),
-            # side stream: q, dO, kd, vd, the float32 dq partial, lse*log2(e), delta read;
-            # dq, dkd, dvd written
-            "diag_bwd": dict(flop=0, diag_flop=10 * diagf,
-                             bytes=(2 * u + 2 * N * u + f32 + 2 * rowf + u + 2 * N * u) if N else 0),
-            # the wait for the side stream: time only
-            "bwd_tail": dict(flop=0, diag_flop=0, bytes=0),
-        })
-    return work
 
 
 class HipEvents:
@@ -217,8 +189,6 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of CPU oracle work for the baseline (0 = skip)")
     ap.add_argument("--no-flush", action="store_true")
-    ap.add_argument("--deterministic", action="store_true",
-                    help="time the split (bitwise-reproducible) backward instead of the fused one")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB before timing (a known-size "
                          "kernel for calibrating the HBM byte counters)")
@@ -245,9 +215,7 @@ def main():
     inp_cpu = synth.make_inputs(w)
     d = {k: v.to(dev) for k, v in inp_cpu.items()}
     prob = e3.Problem(w.B, w.T, w.T_kv, w.H, w.D, w.num_blocks, w.scale, dtype=w.torch_dtype,
-                      layout=w.layout, cp=w.cp, rank=w.rank, cu_seqlens=w.cu_seqlens(), device=dev,
-                      deterministic=args.deterministic)
-    path = "fused" if (w.dtype == "bf16" and not args.deterministic) else "split"
+                      layout=w.layout, cp=w.cp, rank=w.rank, cu_seqlens=w.cu_seqlens(), device=dev)
     P0 = prob.pair_count()                      # per (batch row, head)
     out = torch.empty_like(d["q"])
     lse = torch.empty(w.B, w.H, w.T, dtype=torch.float32, device=dev)
@@ -326,7 +294,7 @@ def main():
     ev.destroy(evb)
     del flush_buf
 
-    work = kernel_work(w, P0, path)
+    work = kernel_work(w, P0)
     kern = {}
     for k in KERNELS:
         t_us = statistics.mean(per[k]) * 1e3
@@ -335,13 +303,12 @@ def main():
             "us_mean": round(t_us, 2), "us_median": round(statistics.median(per[k]) * 1e3, 2),
             "tflops": round(kw["flop"] / (t_us * 1e-6) / 1e12, 2) if kw["flop"] and t_us > 0 else None,
             "gbs": round(kw["bytes"] / (t_us * 1e-6) / 1e9, 1) if kw["bytes"] and t_us > 0 else None,
-            "flop": kw["flop"], "bytes": kw["bytes"], "kernel": KERNEL_NAMES[path][k],
+            "flop": kw["flop"], "bytes": kw["bytes"], "kernel": KERNEL_NAMES[k],
         }
-    kern["diag_bwd"]["stream"] = "side (overlaps bwd_main)"
-    if path == "split":
-        kern["bwd_tail"]["note"] = "time only: the wait for diag_bwd after bwd_main"
+    kern["diag_bwd"]["stream"] = "side (overlaps dkdv)"
+    kern["bwd_tail"]["note"] = "time only: the wait for diag_bwd after dkdv"
     # the dominant kernel: the longest of the kernels on the critical path
-    dom = max(("fwd", "bwd_pre", "bwd_main", "diag_bwd"), key=lambda k: kern[k]["us_mean"])
+    dom = max(("fwd", "dq", "dkdv", "diag_bwd"), key=lambda k: kern[k]["us_mean"])
     dk = kern[dom]
     t_dom = dk["us_mean"] * 1e-6
     peak_t = PEAK_TFLOPS[w.dtype]
@@ -354,8 +321,8 @@ def main():
         roof = {"bound": "hbm", "achieved": round(dk["bytes"] / t_dom / 1e9, 1), "peak": PEAK_GBS,
                 "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = measured_traffic(KERNEL_NAMES[path][dom], w.name)
-    roof["kernel"] = KERNEL_NAMES[path][dom]
+    roof["traffic"] = measured_traffic(KERNEL_NAMES[dom], w.name)
+    roof["kernel"] = KERNEL_NAMES[dom]
     roof["stage"] = dom
     roof["algorithmic"] = {"flop": dk["flop"], "bytes": dk["bytes"]}
 
@@ -377,8 +344,7 @@ def main():
         "data": "synthetic (seeded N(0,1) inputs, resident in HBM)",
         "config": {"workload": w.name, "B": w.B, "T": w.T, "T_kv": w.T_kv, "H": w.H, "D": w.D,
                    "num_blocks": w.num_blocks, "layout": w.layout, "cp": w.cp, "rank": w.rank,
-                   "num_docs": len(w.doc_lens) if w.doc_lens else 1, "seed": w.seed,
-                   "backward": path},
+                   "num_docs": len(w.doc_lens) if w.doc_lens else 1, "seed": w.seed},
         "pct_peak": round(100.0 * value / PEAK_TFLOPS[w.dtype], 2),
         "counted_flop": counted,
         "pairs_P0": P0,

@@ -49,7 +49,7 @@ class _Problem(ctypes.Structure):
         ("cu_seqlens_host", ctypes.POINTER(ctypes.c_int32)),
         ("cu_seqlens_dev", ctypes.c_void_p),
         ("k0_batch_stride", ctypes.c_int64), ("kd_batch_stride", ctypes.c_int64),
-        ("kd_block_stride", ctypes.c_int64), ("deterministic", ctypes.c_int32),
+        ("kd_block_stride", ctypes.c_int64),
     ]
 
 
@@ -146,7 +146,7 @@ class Problem:
     def __init__(self, B: int, T: int, T_kv: int, H: int, D: int, num_blocks: int, scale: float,
                  dtype=torch.bfloat16, layout: str = "full", cp: int = 1, rank: int = 0,
                  cu_seqlens=None, device=None, k0_batch_stride: int = 0,
-                 kd_batch_stride: int = 0, kd_block_stride: int = 0, deterministic: bool = False):
+                 kd_batch_stride: int = 0, kd_block_stride: int = 0):
         if dtype not in DTYPES:
             raise ValueError(f"dtype {dtype} not supported (bfloat16 or float32)")
         if layout not in LAYOUTS:
@@ -184,8 +184,6 @@ class Problem:
         s.k0_batch_stride = k0_batch_stride
         s.kd_batch_stride = kd_batch_stride
         s.kd_block_stride = kd_block_stride
-        s.deterministic = 1 if deterministic else 0
-        self.deterministic = bool(deterministic)
         self._s = s
         # Element strides of the k/v tensors (block 0 and the diagonal blocks) and
         # of their gradients; 0 in the arguments means dense.

@@ -18,7 +18,6 @@
 namespace e3 {
 hipError_t launch_fwd(const Args& a, int dtype, int D, hipStream_t st);
 hipError_t launch_bwd(const Args& a, int dtype, int D, hipStream_t st);
-hipError_t launch_bwd_fused(const Args& a, int D, hipStream_t st);
 hipError_t launch_lse_merge(float* out, float* lse, const float* bo, const float* bl, int B, int T,
                             int H, int D, int blayout, hipStream_t st);
 hipError_t launch_diag_merge(const Args& a, const float* out_acc, const float* lse_acc, int dtype, int D,
@@ -223,9 +222,6 @@ struct BwdWs {
   size_t delta, dqd, total;
 };
 
-// The fused backward (bf16 unless the problem asks for the deterministic path).
-bool fused_path(const e3_problem* p) { return p->dtype == E3_BF16 && !p->deterministic; }
-
 BwdWs bwd_ws_layout(const e3_problem* p) {
   BwdWs l;
   l.pitch = geo_of(p).pitch();
@@ -233,8 +229,7 @@ BwdWs bwd_ws_layout(const e3_problem* p) {
   l.delta = rows * sizeof(float);
   l.dqd = 2 * rows * sizeof(float);
   const int N = p->num_blocks - 1;
-  const bool acc = N > 0 || fused_path(p);
-  l.total = l.dqd + (acc ? (size_t)p->B * p->T * p->H * p->D * sizeof(float) : 0);
+  l.total = l.dqd + (N > 0 ? (size_t)p->B * p->T * p->H * p->D * sizeof(float) : 0);
   return l;
 }
 
@@ -278,7 +273,7 @@ int bwd_impl(const e3_problem* p, const void* dout, const void* q, const void* k
   a.dv0 = dv0;
   a.dkd = dkd;
   a.dvd = dvd;
-  hipError_t e = fused_path(p) ? e3::launch_bwd_fused(a, p->D, st) : e3::launch_bwd(a, p->dtype, p->D, st);
+  hipError_t e = e3::launch_bwd(a, p->dtype, p->D, st);
   if (e != hipSuccess) return fail(E3_EHIP, "backward launch failed: %s", hipGetErrorString(e));
   return ok();
 }
@@ -637,7 +632,6 @@ int eagle3_diag_bwd(const e3_problem* p, const void* dout, const void* q, const 
   }
   timing_reset();
   e3::Args a = make_args(p, r);
-  a.diag_self = 1;
   a.q = q;
   a.kd = kd;
   a.vd = vd;

@@ -59,7 +59,7 @@ struct DkdvCfg {
 // end doc_end(k_hi - 1): per run, rows whose global position lies in
 // [k_lo, dend). Tile starts are aligned to BMQ relative to the run start.
 struct QIter {
-  int run, ls, len, gb, t0, tend;
+  int run, ls, len, gb, t0, tend, pst;
   int qlo, qhi;
   bool valid;
   __device__ void seek(const Geo& g, int BMQ) {
@@ -70,6 +70,7 @@ struct QIter {
       if (lo < hi) {
         t0 = ((lo - gb) / BMQ) * BMQ;   // offset within the run
         tend = hi - gb;
+        pst = (ls + 3) / 4 * 4 + 68 * run;   // = Geo::run_pad_start(run)
         valid = true;
         return;
       }
@@ -92,6 +93,7 @@ struct QIter {
   __device__ int row0() const { return ls + t0; }
   __device__ int nrows(int BMQ) const { return (len - t0) < BMQ ? (len - t0) : BMQ; }
   __device__ int gpos0() const { return gb + t0; }
+  __device__ int prow0() const { return pst + t0; }   // = Geo::prow(row0())
 };
 
 // Waves 0-3 ("P" waves) hold K for their 32 keys and form S = Q K^T, P and
@@ -101,7 +103,11 @@ struct QIter {
 // one overlap the MFMAs of the other. Both kinds run the same MFMA code on
 // different tiles (read along the rows of Q or dO, then down the rows of dO or
 // Q) and share registers.
-template <typename T, int D>
+// KVACC: ring-step mode (only the keys of the launch's ring step, added into
+// float32 accumulators). ZZD: a zig-zag share of several documents (query runs
+// per document). Separate instantiations keep the common one within the
+// registers that let the diagonal-gradient kernel share its SIMDs.
+template <typename T, int D, bool KVACC, bool ZZD>
 __global__ __launch_bounds__(512, 1) void dkdv_kernel(const Args a) {
   using C = DkdvCfg<T, D>;
   using Op = typename V8<T>::type;
@@ -126,7 +132,8 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(const Args a) {
   const int BH = a.B * a.H;
   const int kt = blockIdx.x / BH, bh = blockIdx.x % BH,
             b = bh / a.H, h = bh % a.H;
-  const Geo geo{a.layout, a.cp, a.rank, a.T, a.Tkv, a.cu, a.ndocs};
+  // (the document table matters for the query runs only in a multi-document zig-zag share)
+  const Geo geo{a.layout, a.cp, a.rank, a.T, a.Tkv, ZZD ? a.cu : nullptr, ZZD ? a.ndocs : 1};
   const int kt0 = kt * BNK;
   const int kt1 = (kt0 + BNK) < a.Tkv ? (kt0 + BNK) : a.Tkv;
 
@@ -143,8 +150,8 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(const Args a) {
   // This lane's key; a query at global position gm sees it iff s <= gm < s_hi.
   // In ring-step mode only the keys held at the launch's ring step count.
   const int s = kt0 + kw * 32 + l32;
-  const bool svalid = s < a.Tkv && (!a.kv_accum || geo.in_step(s, a.step_lo));
-  if (a.kv_accum && !__syncthreads_or(svalid)) return;   // no key of the step in this tile
+  const bool svalid = s < a.Tkv && (!KVACC || geo.in_step(s, a.step_lo));
+  if (KVACC && !__syncthreads_or(svalid)) return;   // no key of the step in this tile
   const int s_hi = svalid ? doc_hi_of(a.cu, a.ndocs, s, a.Tkv) : 0;
   Op kv[KS];   // K (P waves) or V (dS waves) of this lane's key
 #pragma unroll
@@ -165,7 +172,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(const Args a) {
   const TileDma<BMQ, C::RRB, C::U, NW> tdma(rrow, w, lane);
   auto dma_stage = [&](int p, const QIter& q) {
     const unsigned st = sbase + (unsigned)(p * C::STAGE);
-    const int r0 = q.row0(), nr = q.nrows(BMQ), p0 = geo.prow(r0);
+    const int r0 = q.row0(), nr = q.nrows(BMQ), p0 = q.prow0();
     tdma(st, qbytes + (long long)r0 * rrow, nr);
     tdma(st + C::RT, obytes + (long long)r0 * rrow, nr);
     if (w == 0 && lane < BMQ / 2) {
@@ -231,7 +238,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(const Args a) {
     }
     Op ops[BMQ / 16];
     if (role == 0) {
-      if (a.kv_accum || !interior(it)) mask(sp, it);   // ring-step mode: keys outside the step are masked
+      if (KVACC || !interior(it)) mask(sp, it);   // ring-step mode: keys outside the step are masked
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -281,7 +288,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(const Args a) {
 
   // dV0 (P waves) or dK0 = scale * dK (dS waves); keys no query sees get zeros.
   // Ring-step mode adds into the float32 accumulators of the step's keys.
-  if (svalid && a.kv_accum) {
+  if (KVACC && svalid) {
     const float f = role ? a.scale : 1.f;
     float* ob = reinterpret_cast<float*>(role ? a.dk0 : a.dv0) + (long long)b * a.k0_bs + (long long)h * D +
                 (long long)s * rs;
@@ -294,7 +301,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(const Args a) {
         for (int i = 0; i < 4; ++i) x[i] += acc[db][4 * jj + i] * f;
         *reinterpret_cast<f32x4*>(ob + 32 * db + 8 * jj + 4 * g) = x;
       }
-  } else if (svalid) {
+  } else if (!KVACC && svalid) {
     const float f = role ? a.scale : 1.f;
     T* ob = reinterpret_cast<T*>(role ? a.dk0 : a.dv0) + (long long)b * a.k0_bs + (long long)h * D +
             (long long)s * rs;
@@ -309,318 +316,6 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(const Args a) {
         *reinterpret_cast<v4*>(ob + 32 * db + 8 * jj + 4 * g) = x;
       }
   }
-}
-
-// ---------------------------------------------------------------------------
-// Fused block-0 backward (bf16): dK0, dV0 and dQ in one pass over the (key
-// tile, query tile) pairs. The split dK/dV + dQ kernels compute S and dP twice
-// (7 products per pair); this kernel computes them once (5 products: S, dP, dV,
-// dK, dQ) and adds each step's dQ into a float32 accumulator with atomic adds,
-// so its result is not bitwise reproducible (the split path is).
-// ---------------------------------------------------------------------------
-template <int D>
-struct FusedCfg {
-  static constexpr int NT = 512;
-  static constexpr int NW = NT / 64;
-  static constexpr int BNK = 128;            // keys per workgroup (32 per wave of each role)
-  static constexpr int BMQ = 64;             // queries per step
-  static constexpr int MB = BMQ / 32;
-  static constexpr int KS = D / 16;
-  static constexpr int DB = D / 32;
-  static constexpr int RRB = D * 2;          // Q, dO and K rows: bytes
-  static constexpr int RT = BMQ * RRB;       // one Q or dO tile
-  static constexpr int STAGE = 2 * RT;       // Q, dO
-  static constexpr int NS = 2;
-  static constexpr int LSTAGE = 2 * BMQ * 4; // lse2, delta
-  static constexpr int PRB = BMQ * 2;        // P / dS tile [key][query]: row bytes
-  static constexpr int PT = BNK * PRB;
-  static constexpr int KT = BNK * RRB;       // the workgroup's K rows (the dQ product reads K^T)
-  static constexpr int NQB = MB * DB;        // 32x32 blocks of one step's dQ
-  static constexpr int KSPLIT = NW / NQB;    // waves per dQ block (they split its keys)
-  static constexpr int KPW = BNK / 16 / KSPLIT;   // 16-key steps of one wave's dQ share
-  static constexpr int LDS = NS * STAGE + NS * LSTAGE + 2 * PT + KT;
-};
-
-__device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
-
-// Roles as in dkdv_kernel: waves 0-3 hold K and form S, P and dV; waves 4-7 hold V
-// and form dP, dS and dK. Step j of the walk over the query tiles that see the
-// workgroup's keys, in two phases with one barrier after each:
-//   phase 1: the copy of tile j+1 starts (into the stage tile j-1 used); every
-//     wave adds one 32x32 block of dQ(j-1) = scale dS(j-1) K (read down the rows
-//     of the dS tile and of the K tile) into the float32 dq; S(j) or dP(j); the P
-//     waves form P(j) and write it, key-major, into the P/dS tile of step j;
-//   barrier (P(j) is visible);
-//   phase 2: the dS waves read P(j), form dS(j) = P(j) (dP(j) - delta) and write it
-//     over P(j); dV += dO^T P, dK += Q^T dS;
-//   barrier (dS(j) and tile j+1 are visible; tile j's stage is free).
-// Two stages and two P/dS tiles: tile j+1 goes where tile j-1 was, whose last
-// reads (dV, dK of step j-1) precede the barrier that ends step j-1; P(j+1)
-// overwrites dS(j-1), whose last reads (dQ(j-1) in phase 1 of step j) precede
-// the barrier that ends step j.
-template <int D>
-__global__ __launch_bounds__(512, 1) void fused_bwd_kernel(const Args a) {
-  using T = bf16;
-  using C = FusedCfg<D>;
-  using Op = bf16x8;
-  constexpr int BNK = C::BNK, BMQ = C::BMQ, MB = C::MB, KS = C::KS, DB = C::DB, NW = C::NW;
-  __shared__ __attribute__((aligned(16))) char smem[C::LDS];
-  char* const lb0 = smem + C::NS * C::STAGE;             // lse2 / delta stages
-  char* const pbuf = lb0 + C::NS * C::LSTAGE;            // two P / dS tiles
-  char* const ktile = pbuf + 2 * C::PT;                  // K rows of the workgroup
-  const unsigned sbase = lds_addr(smem);
-
-  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int role = w >> 2;
-  const int kw = w & 3;
-  if (role == 0) __builtin_amdgcn_s_setprio(2);
-  else __builtin_amdgcn_s_setprio(1);
-  const int BH = a.B * a.H;
-  const int kt = blockIdx.x / BH, bh = blockIdx.x % BH, b = bh / a.H, h = bh % a.H;
-  const Geo geo{a.layout, a.cp, a.rank, a.T, a.Tkv, a.cu, a.ndocs};
-  const int kt0 = kt * BNK;
-  const int kt1 = (kt0 + BNK) < a.Tkv ? (kt0 + BNK) : a.Tkv;
-
-  const long long rs = (long long)a.H * D;
-  const T* kvb = reinterpret_cast<const T*>(role ? a.v0 : a.k0) + (long long)b * a.k0_bs + (long long)h * D;
-  const char* const qbytes = (const char*)uniform64(
-      (unsigned long long)(reinterpret_cast<const T*>(a.q) + (long long)b * a.T * rs + (long long)h * D));
-  const char* const obytes = (const char*)uniform64(
-      (unsigned long long)(reinterpret_cast<const T*>(a.dout) + (long long)b * a.T * rs + (long long)h * D));
-  const char* const kbytes = (const char*)uniform64((unsigned long long)(
-      reinterpret_cast<const T*>(a.k0) + (long long)b * a.k0_bs + (long long)h * D + (long long)kt0 * rs));
-  const char* const lbytes = reinterpret_cast<const char*>(a.lse2 + (long long)bh * a.q_pitch);
-  const unsigned ldoff = (unsigned)((long long)BH * a.q_pitch * 4);
-  const unsigned rrow = (unsigned)(rs * 2);
-  float* const dqa = const_cast<float*>(a.dqd) + (long long)b * a.T * rs + (long long)h * D;
-
-  const int s = kt0 + kw * 32 + l32;
-  const bool svalid = s < a.Tkv;
-  const int s_hi = svalid ? doc_hi_of(a.cu, a.ndocs, s, a.Tkv) : 0;
-  Op kv[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks)
-    kv[ks] = svalid ? load8(kvb + (long long)s * rs + 16 * ks + 8 * g) : zero8<T>();
-  const int hi_min = doc_hi_of(a.cu, a.ndocs, kt0, a.Tkv);
-  const int q_hi = doc_hi_of(a.cu, a.ndocs, kt1 - 1, a.Tkv);
-
-  f32x16 acc[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int j = 0; j < 16; ++j) acc[db][j] = 0.f;
-  const float c2 = a.c2;
-
-  const TileDma<BMQ, C::RRB, 1, NW> tdma(rrow, w, lane);
-  auto dma_stage = [&](int p, const QIter& q) {
-    const unsigned st = sbase + (unsigned)(p * C::STAGE);
-    const int r0 = q.row0(), nr = q.nrows(BMQ), p0 = geo.prow(r0);
-    tdma(st, qbytes + (long long)r0 * rrow, nr);
-    tdma(st + C::RT, obytes + (long long)r0 * rrow, nr);
-    if (w == 0 && lane < BMQ / 2) {
-      const unsigned voff = lane < BMQ / 4 ? 16u * lane : ldoff + 16u * (lane - BMQ / 4);
-      lds_dma16(lbytes + (long long)p0 * 4, voff, sbase + (unsigned)(lb0 - smem) + p * C::LSTAGE);
-    }
-  };
-  auto interior = [&](const QIter& q) {
-    const int gq0 = q.gpos0();
-    return q.nrows(BMQ) == BMQ && kt0 + BNK <= a.Tkv && gq0 >= kt0 + BNK - 1 &&
-           gq0 + BMQ - 1 < hi_min;
-  };
-  auto mask = [&](f32x16 (&sp)[MB], const QIter& q) {
-    const int gq0 = q.gpos0(), nr = q.nrows(BMQ);
-    const int lo = s - gq0 - 4 * g;
-    const int hi = (svalid ? ((nr < s_hi - gq0 ? nr : s_hi - gq0) - 1) : -1) - 4 * g;
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int o = 32 * mb + 8 * (j >> 2) + (j & 3);
-        sp[mb][j] = (o >= lo && o <= hi) ? sp[mb][j] : kNegInf;
-      }
-  };
-  // The P / dS tile holds [key][query] rows of PRB bytes, chunks swizzled; this
-  // lane's key row and, for accumulator elements 4jj..4jj+3 of query block mb,
-  // the 8-byte piece of queries 32mb + 8jj + 4g .. +3.
-  const int prow_k = kw * 32 + l32;
-  auto pslot_off = [&](int mb, int jj) {
-    return prow_k * C::PRB + 16 * ((4 * mb + jj) ^ sw_mask<C::PRB, 1>(prow_k)) + 8 * g;
-  };
-
-  // dQ of one step: this wave's 32x32 block (query block qb, column block db) over
-  // its share of the 128 keys, read down the rows of the dS tile and the K tile;
-  // added with atomics into the float32 dq (rows past the tile's end skipped).
-  const ColRead<T, C::PRB> rds(lane);
-  const ColRead<T, C::RRB> rk(lane);
-  const int blk = w % C::NQB, kpart = w / C::NQB;
-  const int qb = blk % MB, dbq = blk / MB;
-  auto dq_step = [&](const char* dst, int row0, int nrows) {
-    f32x16 c;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) c[j] = 0.f;
-    struct AB { Op x, y; };
-    mfma_ring<C::KPW, 2>(
-        [&](int i) {
-          const int k0 = 16 * (kpart * C::KPW + i);
-          return AB{rds(dst, k0, 32 * qb), rk(ktile, k0, 32 * dbq)};
-        },
-        [&](int i, const AB& op) { mfma16(op.x, op.y, c); });
-    float* const base = dqa + (long long)row0 * rs + 32 * dbq + l32;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int qr = 32 * qb + 8 * (j >> 2) + 4 * g + (j & 3);
-      if (qr < nrows) unsafeAtomicAdd(base + (long long)qr * rs, c[j] * a.scale);
-    }
-  };
-
-  QIter it, i1;
-  it.begin(geo, kt0, q_hi, BMQ);
-  i1 = it;
-  if (i1.valid) i1.next(geo, BMQ);
-  {
-    const TileDma<BNK, C::RRB, 1, NW> kdma(rrow, w, lane);
-    kdma(sbase + (unsigned)(ktile - smem), kbytes, kt1 - kt0);
-  }
-  if (it.valid) dma_stage(0, it);
-  wait_all();
-  __syncthreads();
-
-  const ColRead<T, C::RRB> rcol(lane);
-  int cur = 0;
-  int prev_row0 = 0, prev_nrows = 0;
-  bool have_prev = false;
-  while (it.valid) {
-    if (i1.valid) dma_stage(cur ^ 1, i1);
-    const char* const st = smem + cur * C::STAGE;
-    const float* const L2s = reinterpret_cast<const float*>(lb0 + cur * C::LSTAGE);
-    const float* const Ds = L2s + BMQ;
-    char* const slot = pbuf + cur * C::PT;
-    // ---- phase 1 ----
-    if (have_prev) dq_step(pbuf + (cur ^ 1) * C::PT, prev_row0, prev_nrows);
-    f32x16 sp[MB];
-    {
-      const char* const R = st + role * C::RT;
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) sp[mb][j] = 0.f;
-      mfma_ring<KS * MB, 3>(
-          [&](int i) { return lds_sw8<T, C::RRB>(R, 32 * (i % MB) + l32, 16 * (i / MB) + 8 * g); },
-          [&](int i, const Op& op) { mfma16(op, kv[i / MB], sp[i % MB]); });
-    }
-    Op ops[BMQ / 16];
-    if (role == 0) {
-      if (!interior(it)) mask(sp, it);
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(L2s + 32 * mb + 8 * jj + 4 * g);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) sp[mb][4 * jj + i] = fast_exp2(fmaf(sp[mb][4 * jj + i], c2, -l4[i]));
-          bf16x4 p4;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) p4[i] = (bf16)sp[mb][4 * jj + i];
-          *reinterpret_cast<bf16x4*>(slot + pslot_off(mb, jj)) = p4;
-        }
-#pragma unroll
-      for (int q = 0; q < BMQ / 16; ++q) ops[q] = to_op(sp[q >> 1], 8 * (q & 1), T());
-    }
-    wait_lds();
-    __syncthreads();   // P(j) is visible
-    // ---- phase 2 ----
-    if (role == 1) {
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const bf16x4 p4 = *reinterpret_cast<const bf16x4*>(slot + pslot_off(mb, jj));
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(Ds + 32 * mb + 8 * jj + 4 * g);
-          bf16x4 s4;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            sp[mb][4 * jj + i] = (float)p4[i] * (sp[mb][4 * jj + i] - d4[i]);
-            s4[i] = (bf16)sp[mb][4 * jj + i];
-          }
-          *reinterpret_cast<bf16x4*>(slot + pslot_off(mb, jj)) = s4;
-        }
-#pragma unroll
-      for (int q = 0; q < BMQ / 16; ++q) ops[q] = to_op(sp[q >> 1], 8 * (q & 1), T());
-    }
-    {
-      const char* const Cc = st + (1 - role) * C::RT;
-#pragma unroll
-      for (int ks = 0; ks < BMQ / 16; ++ks)
-#pragma unroll
-        for (int db = 0; db < DB; ++db) mfma16(rcol(Cc, 16 * ks, 32 * db), ops[ks], acc[db]);
-    }
-    wait_all();
-    __syncthreads();   // dS(j) and tile j+1 are visible; tile j's stage is free
-    have_prev = true;
-    prev_row0 = it.row0();
-    prev_nrows = it.nrows(BMQ);
-    it = i1;
-    if (i1.valid) i1.next(geo, BMQ);
-    cur ^= 1;
-  }
-  if (have_prev) dq_step(pbuf + (cur ^ 1) * C::PT, prev_row0, prev_nrows);
-
-  if (svalid) {
-    const float f = role ? a.scale : 1.f;
-    T* ob = reinterpret_cast<T*>(role ? a.dk0 : a.dv0) + (long long)b * a.k0_bs + (long long)h * D +
-            (long long)s * rs;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        bf16x4 x;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) x[i] = (bf16)(acc[db][4 * jj + i] * f);
-        *reinterpret_cast<bf16x4*>(ob + 32 * db + 8 * jj + 4 * g) = x;
-      }
-  }
-}
-
-// delta = <dO, O> and lse2 = lse * log2(e) of one 64-row chunk of one run of the
-// local rows of one (b, h), in the padded layout (rows past the run's end get 0),
-// and zeros in the float32 dq accumulator rows the fused kernel adds into.
-template <typename T, int D>
-__global__ __launch_bounds__(256) void bwd_prep_kernel(const Args a) {
-  constexpr int LPR = D / 8, RPP = 256 / LPR;
-  const int tid = threadIdx.x, cc = (tid % LPR) * 8;
-  const int BH = a.B * a.H;
-  const int tile = blockIdx.x / BH, bh = blockIdx.x % BH, b = bh / a.H, h = bh % a.H;
-  const Geo geo{a.layout, a.cp, a.rank, a.T, a.Tkv, a.cu, a.ndocs};
-  int row0, nrows, gpos0;
-  geo.qtile(tile, 64, row0, nrows, gpos0);
-  const long long p0 = (long long)bh * a.q_pitch + geo.prow(row0);
-  const long long rs = (long long)a.H * D;
-  for (int r = tid / LPR; r < 64; r += RPP) {
-    const bool valid = r < nrows;
-    float dl = 0.f, l2 = 0.f;
-    if (valid) {
-      const long long off = ((long long)b * a.T + row0 + r) * rs + (long long)h * D + cc;
-      dl = group_sum<LPR>(dot8(load8(reinterpret_cast<const T*>(a.dout) + off),
-                               load8(reinterpret_cast<const T*>(a.o_in) + off), 0.f));
-      l2 = a.lse_in[(long long)bh * a.T + row0 + r] * kLog2e;
-      f32x8 z;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) z[e] = 0.f;
-      *reinterpret_cast<f32x8*>(const_cast<float*>(a.dqd) + off) = z;
-    }
-    if ((tid % LPR) == 0) {
-      a.lse2[p0 + r] = l2;
-      a.delta[p0 + r] = dl;
-    }
-  }
-}
-
-// dq = the float32 accumulator converted to q's dtype.
-template <typename T>
-__global__ __launch_bounds__(256) void dq_convert_kernel(const float* src, T* dst, long long n8) {
-  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n8; i += (long long)gridDim.x * 256)
-    store8f(dst + 8 * i, *reinterpret_cast<const f32x8*>(src + 8 * i));
 }
 
 // ---------------------------------------------------------------------------
@@ -847,11 +542,18 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void dq_kernel(const A
 // the rows. It only reads q, dO, lse2, delta, kd, vd, so it runs on a side
 // stream next to the dK/dV kernel, whose CUs it shares (few registers, no LDS).
 // ---------------------------------------------------------------------------
-template <typename T, int D>
+// MODE: 0 = the float32 block-0 dq partial from the workspace; 1 = ring-step mode
+// (delta and lse*log2(e) formed here from the merged out/lse; the partial is the
+// caller's float32 accumulator); 2 = no-allocation backward (the block-0 dq read
+// back from dq itself, in q's dtype). Separate instantiations keep the default
+// one's registers low enough to share the SIMDs with the dK/dV kernel.
+template <typename T, int D, int MODE>
 __global__ __launch_bounds__(256, 4) void diag_bwd_kernel(const Args a) {
   constexpr int LPR = D / 8;
   constexpr int GPB = 256 / LPR;           // row groups per workgroup
-  constexpr int NB = sizeof(T) == 2 ? 4 : 2;   // blocks per load group (fits 128 VGPRs)
+  // blocks per load group: 4 keeps the kernel within 120 VGPRs, so one of its
+  // waves fits on each SIMD beside the two dK/dV waves (2 x 192 + 120 = 504)
+  constexpr int NB = sizeof(T) == 2 ? 4 : 2;
   using V = typename V8<T>::type;
   const Geo geo{a.layout, a.cp, a.rank, a.T, a.Tkv, a.cu, a.ndocs};
   const int tid = threadIdx.x, cc = (tid % LPR) * 8;
@@ -868,7 +570,7 @@ __global__ __launch_bounds__(256, 4) void diag_bwd_kernel(const Args a) {
     const V qv = load8(reinterpret_cast<const T*>(a.q) + qoff);
     const V ov = load8(reinterpret_cast<const T*>(a.dout) + qoff);
     float l2, dl;
-    if (a.diag_self) {
+    if constexpr (MODE == 1) {
       // ring-step mode: delta = <dO, O> and lse*log2(e) formed here from the merged out/lse
       const V oo = load8(reinterpret_cast<const T*>(a.o_in) + qoff);
       dl = group_sum<LPR>(dot8(ov, oo, 0.f));
@@ -877,17 +579,10 @@ __global__ __launch_bounds__(256, 4) void diag_bwd_kernel(const Args a) {
       l2 = a.lse2[loff];
       dl = a.delta[loff];
     }
-    // scale * dQ(block 0): the float32 partial, or (dq_in_out) dq itself in q's
-    // dtype; with the fused block-0 kernel (dq_atomic) only the diagonal part is
-    // formed here and added into the float32 accumulator
+    // scale * dQ(block 0): the float32 partial, or (MODE 2) dq itself in q's dtype
     f32x8 dq;
-    if (a.dq_atomic) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) dq[e] = 0.f;
-    } else {
-      dq = a.dq_in_out ? load8f(reinterpret_cast<const T*>(a.dq) + qoff)
-                       : *reinterpret_cast<const f32x8*>(a.dqd + qoff);
-    }
+    if constexpr (MODE == 2) dq = load8f(reinterpret_cast<const T*>(a.dq) + qoff);
+    else dq = *reinterpret_cast<const f32x8*>(a.dqd + qoff);
     for (int i0 = 0; i0 < a.N; i0 += NB) {
       const int n = (a.N - i0) < NB ? (a.N - i0) : NB;
       // Unconditional loads (block index clamped), all issued before any use.
@@ -919,13 +614,7 @@ __global__ __launch_bounds__(256, 4) void diag_bwd_kernel(const Args a) {
         }
       }
     }
-    if (a.dq_atomic) {
-      float* const acc = const_cast<float*>(a.dqd) + qoff;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) unsafeAtomicAdd(acc + e, dq[e]);
-    } else {
-      store8f(reinterpret_cast<T*>(a.dq) + qoff, dq);
-    }
+    store8f(reinterpret_cast<T*>(a.dq) + qoff, dq);
   }
 }
 
@@ -950,7 +639,7 @@ static hipError_t launch_bwd_t(const Args& a, hipStream_t st) {
     hipStream_t side = nullptr;
     if ((e = side_begin(st, 0, side)) != hipSuccess) return e;
     timing_mark(side);
-    hipLaunchKernelGGL((diag_bwd_kernel<T, D>), dim3(kDiagGrid), dim3(256), 0, side, a);
+    hipLaunchKernelGGL((diag_bwd_kernel<T, D, 0>), dim3(kDiagGrid), dim3(256), 0, side, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     timing_mark(side);
   } else {
@@ -959,14 +648,20 @@ static hipError_t launch_bwd_t(const Args& a, hipStream_t st) {
   }
   const long long nk = (long long)((a.Tkv + DkdvCfg<T, D>::BNK - 1) / DkdvCfg<T, D>::BNK) * a.B * a.H;
   if (nk > 0) {
-    hipLaunchKernelGGL((dkdv_kernel<T, D>), dim3((unsigned)nk), dim3(DkdvCfg<T, D>::NT), 0, st, a);
+    const bool zzd = a.layout == LAYOUT_ZIGZAG && a.ndocs > 1;
+    if (a.kv_accum)
+      hipLaunchKernelGGL((dkdv_kernel<T, D, true, true>), dim3((unsigned)nk), dim3(DkdvCfg<T, D>::NT), 0, st, a);
+    else if (zzd)
+      hipLaunchKernelGGL((dkdv_kernel<T, D, false, true>), dim3((unsigned)nk), dim3(DkdvCfg<T, D>::NT), 0, st, a);
+    else
+      hipLaunchKernelGGL((dkdv_kernel<T, D, false, false>), dim3((unsigned)nk), dim3(DkdvCfg<T, D>::NT), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   timing_mark(st);
   if (a.N > 0 && a.dq_in_out) {
     // no-allocation backward: the diagonal gradients after dK/dV on the same stream
     // (they read the block-0 dq the dQ kernel left in dq)
-    hipLaunchKernelGGL((diag_bwd_kernel<T, D>), dim3(kDiagGrid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((diag_bwd_kernel<T, D, 2>), dim3(kDiagGrid), dim3(256), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   } else if (a.N > 0 && (e = side_end(st, 0)) != hipSuccess) {
     return e;
@@ -975,64 +670,12 @@ static hipError_t launch_bwd_t(const Args& a, hipStream_t st) {
   return hipSuccess;
 }
 
-// Fused path (bf16), with the timing hook's marks m0..m5:
-//   main:  m0 prep (delta, lse2, dq accumulator zeroed) m1 | fused dK/dV/dQ m4 |
-//          join, dq converted m5
-//   side:        (forked at m1) m2 diagonal gradients (dq part added atomically) m3
-template <int D>
-static hipError_t launch_bwd_fused_t(const Args& a, hipStream_t st) {
-  const Geo geo{a.layout, a.cp, a.rank, a.T, a.Tkv, a.cu_host, a.ndocs};
-  const long long nrow = (long long)a.B * a.H * a.q_pitch;
-  if (nrow == 0) return hipSuccess;
-  hipError_t e;
-  timing_mark(st);
-  const long long np = (long long)geo.ntiles(64) * a.B * a.H;
-  if (np > 0) {
-    hipLaunchKernelGGL((bwd_prep_kernel<bf16, D>), dim3((unsigned)np), dim3(256), 0, st, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
-  timing_mark(st);
-  Args ad = a;
-  ad.dq_atomic = 1;
-  if (a.N > 0) {
-    hipStream_t side = nullptr;
-    if ((e = side_begin(st, 0, side)) != hipSuccess) return e;
-    timing_mark(side);
-    hipLaunchKernelGGL((diag_bwd_kernel<bf16, D>), dim3(kDiagGrid), dim3(256), 0, side, ad);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    timing_mark(side);
-  } else {
-    timing_mark(st);
-    timing_mark(st);
-  }
-  const long long nk = (long long)((a.Tkv + FusedCfg<D>::BNK - 1) / FusedCfg<D>::BNK) * a.B * a.H;
-  if (nk > 0) {
-    hipLaunchKernelGGL((fused_bwd_kernel<D>), dim3((unsigned)nk), dim3(FusedCfg<D>::NT), 0, st, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
-  timing_mark(st);
-  if (a.N > 0 && (e = side_end(st, 0)) != hipSuccess) return e;
-  const long long n8 = (long long)a.B * a.T * a.H * D / 8;
-  if (n8 > 0) {
-    const long long grid = (n8 + 255) / 256 < 4096 ? (n8 + 255) / 256 : 4096;
-    hipLaunchKernelGGL((dq_convert_kernel<bf16>), dim3((unsigned)grid), dim3(256), 0, st, a.dqd,
-                       reinterpret_cast<bf16*>(a.dq), n8);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
-  timing_mark(st);
-  return hipSuccess;
-}
-
-hipError_t launch_bwd_fused(const Args& a, int D, hipStream_t st) {
-  return D == 128 ? launch_bwd_fused_t<128>(a, st) : launch_bwd_fused_t<64>(a, st);
-}
-
 // Ring-step mode: the closed-form diagonal gradients alone, on the caller's
 // stream, with delta and lse*log2(e) formed in the kernel (diag_self).
 template <typename T, int D>
 static hipError_t launch_diag_bwd_t(const Args& a, hipStream_t st) {
   if ((long long)a.B * a.T * a.H == 0) return hipSuccess;
-  hipLaunchKernelGGL((diag_bwd_kernel<T, D>), dim3(kDiagGrid), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((diag_bwd_kernel<T, D, 1>), dim3(kDiagGrid), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -61,13 +61,9 @@ struct Args {
   int out_f32;          //   the forward writes a float32 (out, lse) of those keys
   int dq_accum;         //   the dQ kernel adds scale * dQ into a float32 dq (dqd)
   int kv_accum;         //   dK/dV adds into float32 dk0/dv0 for the steps' keys only
-  int diag_self;        //   the diagonal kernel forms delta and lse*log2(e) itself
   // No-allocation backward: the block-0 dq goes through dq itself (q's dtype) instead
   // of a float32 workspace partial, and every kernel runs on the caller's stream.
   int dq_in_out;
-  // Fused backward: the diagonal kernel adds its part of dq into the float32
-  // accumulator dqd with atomic adds (the fused block-0 kernel adds the rest).
-  int dq_atomic;
 };
 
 

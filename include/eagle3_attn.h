@@ -110,11 +110,6 @@ typedef struct e3_problem {
   int64_t k0_batch_stride;  /* elements between batch rows of k0/v0/dk0/dv0; 0 = T_kv*H*D */
   int64_t kd_batch_stride;  /* elements between batch rows of kd/vd/dkd/dvd; 0 = N*T*H*D */
   int64_t kd_block_stride;  /* elements between blocks of kd/vd/dkd/dvd; 0 = T*H*D */
-  int32_t deterministic;    /* backward path: 0 = fused (bf16: dK, dV and dQ in one kernel,
-                               dQ accumulated with float32 atomic adds, so dq is not bitwise
-                               reproducible); 1 = split dQ and dK/dV kernels, every output
-                               element written once, bitwise reproducible. float32 problems
-                               always take the split path. */
 } e3_problem;
 
 /* Version of this header's ABI (EAGLE3_ABI_VERSION). Bindings refuse a mismatch rather
@@ -128,9 +123,9 @@ const char* eagle3_last_error(void);
 /* Bytes of device workspace eagle3_attn_bwd / eagle3_shard_bwd need: delta = rowsum(dO*O)
  * and lse*log2(e) (float32 [B, H, P]: P = T for one run of local rows; with the zig-zag
  * layout each chunk of each document is a run, placed at a 16-byte boundary and padded
- * to 64 rows, P < T + 68 * runs + 128), then, when num_blocks > 1 or on the fused path,
- * a float32 [B, T, H, D] dq accumulator. 0 when T == 0. Returns 0 and sets the last
- * error for an invalid problem. */
+ * to 64 rows, P < T + 68 * runs + 128), then, when num_blocks > 1, the block-0 part of
+ * dq (float32 [B, T, H, D]). 0 when T == 0. Returns 0 and sets the last error for an
+ * invalid problem. */
 size_t eagle3_bwd_workspace_bytes(const e3_problem* p);
 
 /* Forward of the full sequence (layout FULL or HEADSHARD):
@@ -150,9 +145,8 @@ int eagle3_attn_bwd(const e3_problem* p, const void* dout, const void* q, const 
 
 /* Backward that allocates nothing, for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid
- * hipMalloc): eagle3_shard_bwd's computation on its split (deterministic) path, for
- * any layout, with no workspace argument (the problem's `deterministic` field is
- * not consulted). delta and lse*log2(e) live in a static device array of
+ * hipMalloc): eagle3_shard_bwd's computation for any layout, with no workspace
+ * argument. delta and lse*log2(e) live in a static device array of
  * eagle3_bwd_noalloc_max_scratch_bytes() = 16 MiB that the library holds on every GPU
  * it runs on until the process ends (2 x B*H*P floats must fit: P as for
  * eagle3_bwd_workspace_bytes; larger problems are refused with E3_EINVAL). The

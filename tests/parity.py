@@ -32,16 +32,15 @@ def inputs(w: synth.Workload) -> dict:
     return synth.make_inputs(w)
 
 
-def problem(w: synth.Workload, device="cuda", deterministic: bool = False) -> e3.Problem:
+def problem(w: synth.Workload, device="cuda") -> e3.Problem:
     return e3.Problem(w.B, w.T, w.T_kv, w.H, w.D, w.num_blocks, w.scale, dtype=w.torch_dtype,
                       layout=w.layout, cp=w.cp, rank=w.rank, cu_seqlens=w.cu_seqlens(),
-                      device=device, deterministic=deterministic)
+                      device=device)
 
 
-def run_hip(w: synth.Workload, inp: dict, device="cuda", deterministic: bool = False):
-    """Forward + backward through the C ABI; the backward takes the fused path
-    (bf16) unless `deterministic` asks for the split one."""
-    prob = problem(w, device, deterministic)
+def run_hip(w: synth.Workload, inp: dict, device="cuda"):
+    """Forward + backward through the C ABI."""
+    prob = problem(w, device)
     d = {k: v.to(device) for k, v in inp.items()}
     out, lse = e3.fwd(prob, d["q"], d["k0"], d["v0"], d["kd"], d["vd"])
     grads = e3.bwd(prob, d["dout"], d["q"], d["k0"], d["v0"], d["kd"], d["vd"], out, lse)

@@ -24,7 +24,6 @@ namespace e3 {
 // Stub launchers: the sanitizer build has no device code.
 hipError_t launch_fwd(const Args&, int, int, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_bwd(const Args&, int, int, hipStream_t) { return hipErrorNotSupported; }
-hipError_t launch_bwd_fused(const Args&, int, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_lse_merge(float*, float*, const float*, const float*, int, int, int, int, int, hipStream_t) {
   return hipErrorNotSupported;
 }
@@ -61,7 +60,6 @@ int main(int argc, char** argv) {
     p.layout = uni(0, 4);                               // 4 is invalid
     p.cp = uni(1, 5);
     p.rank = uni(0, 20) == 0 ? p.cp : uni(0, p.cp - 1);
-    p.deterministic = uni(0, 1);
     const int unit = p.layout == 2 ? 2 * p.cp : (p.layout == 1 ? p.cp : 1);
     int S = unit * uni(0, 160 / unit + 1) + (uni(0, 12) == 0 ? 1 : 0);
     p.B = (p.layout == 2 || uni(0, 1)) ? 1 : uni(1, 3);

@@ -113,14 +113,7 @@ def test_workspace_bytes():
     # and, with diagonal blocks, the block-0 part of dq (float32 [B, T, H, D])
     P = 1024
     assert p.workspace_bytes() == 2 * 1 * 3 * P * 4 + 1 * 1000 * 3 * 128 * 4
-    # the fused bf16 path always needs the float32 dq accumulator; the split
-    # (deterministic) path only with diagonal blocks
-    assert prob(B=1, T=1000, T_kv=1000, H=3, num_blocks=1).workspace_bytes() == \
-        2 * 3 * P * 4 + 1000 * 3 * 128 * 4
-    assert prob(B=1, T=1000, T_kv=1000, H=3, num_blocks=1, deterministic=True).workspace_bytes() == \
-        2 * 3 * P * 4
-    assert prob(B=1, T=1000, T_kv=1000, H=3, num_blocks=1, dtype=torch.float32).workspace_bytes() == \
-        2 * 3 * P * 4
+    assert prob(B=1, T=1000, T_kv=1000, H=3, num_blocks=1).workspace_bytes() == 2 * 3 * P * 4
     # zig-zag: each of the two local chunks is padded to 64 rows on its own
     # zig-zag: run i (of 150 rows) starts at roundup4(local start) + 68 i: 0 and
     # 152 + 68 = 220, and ends its padding at 220 + 192 = 412, rounded up to 448

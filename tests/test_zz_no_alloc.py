@@ -1,6 +1,6 @@
 """The backward that allocates nothing (eagle3_bwd_noalloc, for callers that cannot
 allocate device memory) against the backward with a workspace whose kernels it
-shares (eagle3_shard_bwd on the split, deterministic path): two calls in a row,
+shares (eagle3_shard_bwd): two calls in a row,
 the second with a smaller input, each compared at the parity tolerances; the
 K/V and diagonal gradients come from the same kernels and must be bitwise equal,
 dq differs only by the rounding of its block-0 part to q's dtype."""
@@ -19,7 +19,7 @@ W = synth.small_workload
 def run_both(w):
     inp = inputs(w)
     d = {k: v.cuda() for k, v in inp.items()}
-    prob = problem(w, deterministic=True)
+    prob = problem(w)
     out, lse = e3.fwd(prob, d["q"], d["k0"], d["v0"], d["kd"], d["vd"])
     ref = e3.bwd(prob, d["dout"], d["q"], d["k0"], d["v0"], d["kd"], d["vd"], out, lse)
     grads = tuple(torch.full_like(g, float("nan")) for g in ref)

@@ -1,7 +1,8 @@
 """GPU parity at sizes the oracle finishes in seconds: the HIP path (through the
 C ABI) against the CPU oracle, element by element, on the same seeded inputs.
 Cases span several tiles, ragged tails, single-row sequences, several documents
-(one empty), one-row documents, num_blocks = 1, B > 1, both head dims and every layout."""
+(one empty), one-row documents, num_blocks = 1, B > 1, both head dims, every layout,
+and grids longer than one wave of resident workgroups."""
 import numpy as np
 import pytest
 import torch
@@ -48,6 +49,12 @@ CASES = {
                          doc_lens=[260, 4, 696]),
     "zigzag_docs_f32": W(dtype="f32", S=480, H=2, D=64, num_blocks=3, layout="zigzag", cp=3,
                          rank=2, doc_lens=[60, 6, 414]),
+    # grids several times longer than one wave of resident workgroups
+    "wide_grid_bf16": W(S=260, H=180, D=128, num_blocks=4),
+    "wide_grid_bf16_d64": W(S=140, H=260, D=64, num_blocks=2),
+    "wide_grid_f32": W(dtype="f32", S=150, H=270, D=64, num_blocks=3),
+    "wide_grid_zigzag_docs": W(S=1024, H=136, D=128, num_blocks=3, layout="zigzag", cp=2, rank=1,
+                               doc_lens=[300, 4, 720]),
 }
 
 

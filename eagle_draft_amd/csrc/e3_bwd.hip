@@ -671,7 +671,7 @@ static hipError_t launch_bwd_t(const Args& a, hipStream_t st) {
 }
 
 // Ring-step mode: the closed-form diagonal gradients alone, on the caller's
-// stream, with delta and lse*log2(e) formed in the kernel (diag_self).
+// stream, with delta and lse*log2(e) formed in the kernel (mode 1).
 template <typename T, int D>
 static hipError_t launch_diag_bwd_t(const Args& a, hipStream_t st) {
   if ((long long)a.B * a.T * a.H == 0) return hipSuccess;

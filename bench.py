@@ -179,6 +179,164 @@ def cpu_baseline(w, inp, P0_per_head, budget_s):
     }
 
 
+def _median_us(fn, n=20, warm=3):
+    """Median duration of fn() in microseconds, torch events on the current stream
+    (every entry point timed here launches on it)."""
+    import torch
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(n):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b) * 1e3)
+    return statistics.median(ts)
+
+
+def _roof(kind, amount, us):
+    """Roofline record: kind "mfma" (amount = FLOP, bf16 peak) or "hbm" (bytes)."""
+    if kind == "mfma":
+        ach = amount / (us * 1e-6) / 1e12
+        return {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_TFLOPS["bf16"],
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_TFLOPS["bf16"], 4)}
+    ach = amount / (us * 1e-6) / 1e9
+    return {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_GBS, "unit": "GB/s",
+            "frac": round(ach / PEAK_GBS, 4)}
+
+
+def run_extras(args, dev):
+    """The paths beside the headline, each at a full-size shape, one JSON line each:
+    ring-step mode and the one-pass shard on the last rank of a contiguous ring
+    (cp = 8 of a 32768-token sequence, H = 32, D = 128, num_blocks = 8), the
+    frozen-target forward on the same share (num_blocks = 1, head-major), and the
+    four Ulysses transforms at the Ulysses sequence shard (S_local = 4096 of 32768,
+    H = 32, D = 128, uly = 8). FLOP are counted as in the headline (4*B*H*D*P0
+    forward, 2.5x that backward); bytes are those each kernel must move."""
+    import torch
+    import eagle_draft_amd as e3
+    import synth
+
+    def emit(rec):
+        print(json.dumps(rec), flush=True)
+
+    # ---- ring-step mode against the one-pass shard -----------------------------
+    w = synth.Workload("ring_contig_r7", "bf16", 1, 32768, 32, 128, 8, layout="contiguous",
+                       cp=8, rank=7, seed=args.seed)
+    log(f"[extras] {w}")
+    d = {k: v.to(dev) for k, v in synth.make_inputs(w).items()}
+    prob = e3.Problem(w.B, w.T, w.T_kv, w.H, w.D, w.num_blocks, w.scale, dtype=w.torch_dtype,
+                      layout=w.layout, cp=w.cp, rank=w.rank, device=dev)
+    P0 = prob.pair_count()
+    ffwd = 4.0 * w.B * w.H * w.D * P0
+    out, lse = e3.fwd(prob, d["q"], d["k0"], d["v0"], d["kd"], d["vd"])
+    ws = torch.empty(max(prob.workspace_bytes(), 256), dtype=torch.uint8, device=dev)
+    g = e3.bwd(prob, d["dout"], d["q"], d["k0"], d["v0"], d["kd"], d["vd"], out, lse, workspace=ws)
+    t_fwd = _median_us(lambda: e3.fwd(prob, d["q"], d["k0"], d["v0"], d["kd"], d["vd"], out=out, lse=lse))
+    t_bwd = _median_us(lambda: e3.bwd(prob, d["dout"], d["q"], d["k0"], d["v0"], d["kd"], d["vd"], out,
+                                      lse, grads=g, workspace=ws))
+    B, T, H, D = w.B, w.T, w.H, w.D
+    acc_o = torch.empty(B, T, H, D, dtype=torch.float32, device=dev)
+    acc_l = torch.empty(B, H, T, dtype=torch.float32, device=dev)
+    so = torch.empty_like(acc_o)
+    sl = torch.empty_like(acc_l)
+    o2, l2 = torch.empty_like(out), torch.empty_like(lse)
+    dq_acc = torch.empty(B, T, H, D, dtype=torch.float32, device=dev)
+    dk_acc = torch.empty(B, w.T_kv, H, D, dtype=torch.float32, device=dev)
+    dv_acc = torch.empty_like(dk_acc)
+    gd = (torch.empty_like(d["q"]), torch.empty_like(d["kd"]), torch.empty_like(d["vd"]))
+
+    def ring_fwd():
+        acc_o.zero_()
+        acc_l.fill_(float("-inf"))
+        for j in range(w.cp):
+            e3.ring_fwd_step(prob, j, d["q"], d["k0"], d["v0"], out_step=so, lse_step=sl)
+            e3.lse_merge(acc_o, acc_l, so, sl)
+        e3.diag_merge_fwd(prob, d["q"], d["kd"], d["vd"], acc_o, acc_l, out=o2, lse=l2)
+
+    def ring_bwd():
+        dq_acc.zero_()
+        dk_acc.zero_()
+        dv_acc.zero_()
+        for j in range(w.cp):
+            e3.ring_bwd_step(prob, j, d["dout"], d["q"], d["k0"], d["v0"], out, lse, dq_acc, dk_acc,
+                             dv_acc, workspace=ws)
+        e3.diag_bwd(prob, d["dout"], d["q"], d["kd"], d["vd"], out, lse, dq_acc, grads=gd)
+
+    t_rf = _median_us(ring_fwd, n=10)
+    t_rb = _median_us(ring_bwd, n=10)
+    # the HBM-bound pieces of the chain, alone
+    ring_fwd()
+    t_merge = _median_us(lambda: e3.lse_merge(acc_o, acc_l, so, sl))
+    t_dmerge = _median_us(lambda: e3.diag_merge_fwd(prob, d["q"], d["kd"], d["vd"], acc_o, acc_l, out=o2,
+                                                    lse=l2))
+    t_dbwd = _median_us(lambda: e3.diag_bwd(prob, d["dout"], d["q"], d["kd"], d["vd"], out, lse, dq_acc,
+                                            grads=gd))
+    u = B * T * H * D
+    N = w.N
+    merge_bytes = 3 * u * 4 + 3 * B * H * T * 4
+    dmerge_bytes = u * 2 + 2 * N * u * 2 + u * 4 + B * H * T * 4 + u * 2 + B * H * T * 4
+    dbwd_bytes = 3 * u * 2 + 2 * N * u * 2 + u * 4 + B * H * T * 4 + u * 2 + 2 * N * u * 2
+    cfg = {"workload": w.name, "B": B, "T": T, "T_kv": w.T_kv, "H": H, "D": D, "num_blocks": w.num_blocks,
+           "layout": w.layout, "cp": w.cp, "rank": w.rank}
+    emit({"extra": "ring_step_mode", "metric": "fwd+bwd TFLOP/s (causal), ring steps chained",
+          "value": round(3.5 * ffwd / ((t_rf + t_rb) * 1e-6) / 1e12, 2), "unit": "TFLOP/s",
+          "ms_fwd": round(t_rf / 1e3, 3), "ms_bwd": round(t_rb / 1e3, 3),
+          "one_pass": {"value": round(3.5 * ffwd / ((t_fwd + t_bwd) * 1e-6) / 1e12, 2),
+                       "ms_fwd": round(t_fwd / 1e3, 3), "ms_bwd": round(t_bwd / 1e3, 3)},
+          "roofline": _roof("mfma", 3.5 * ffwd, t_rf + t_rb), "config": cfg, "pairs_P0": P0,
+          "pieces": {"lse_merge": {"us": round(t_merge, 1), "roofline": _roof("hbm", merge_bytes, t_merge)},
+                     "diag_merge_fwd": {"us": round(t_dmerge, 1),
+                                        "roofline": _roof("hbm", dmerge_bytes, t_dmerge)},
+                     "diag_bwd": {"us": round(t_dbwd, 1), "roofline": _roof("hbm", dbwd_bytes, t_dbwd)}},
+          "dtype": "bf16", "data": "synthetic (seeded N(0,1) inputs, resident in HBM)"})
+
+    # ---- frozen-target forward (head-major, num_blocks = 1) ---------------------
+    p1 = e3.Problem(B, T, w.T_kv, H, D, 1, w.scale, dtype=w.torch_dtype, layout=w.layout, cp=w.cp,
+                    rank=w.rank, device=dev)
+    hm = lambda t: t.permute(0, 2, 1, 3).contiguous()
+    qh, kh, vh = hm(d["q"]), hm(d["k0"]), hm(d["v0"])
+    oh, lh = e3.target_cp_fwd(p1, qh, kh, vh)
+    t_tcp = _median_us(lambda: e3.target_cp_fwd(p1, qh, kh, vh, out=oh, lse=lh))
+    emit({"extra": "target_cp_fwd", "metric": "forward TFLOP/s (causal), head-major, num_blocks = 1",
+          "value": round(ffwd / (t_tcp * 1e-6) / 1e12, 2), "unit": "TFLOP/s", "ms": round(t_tcp / 1e3, 3),
+          "roofline": _roof("mfma", ffwd, t_tcp), "config": dict(cfg, num_blocks=1), "pairs_P0": P0,
+          "dtype": "bf16", "data": "synthetic (seeded N(0,1) inputs, resident in HBM)"})
+    del d, out, lse, g, ws, acc_o, acc_l, so, sl, o2, l2, dq_acc, dk_acc, dv_acc, gd, qh, kh, vh, oh, lh
+    torch.cuda.empty_cache()
+
+    # ---- Ulysses transforms -------------------------------------------------------
+    uly, Sl = 8, 4096
+    gen = torch.Generator(device="cpu").manual_seed(args.seed)
+    x = torch.randn(B, Sl, H, D, generator=gen).to(torch.bfloat16).to(dev)
+    lx = torch.randn(B, H, Sl, generator=gen).to(dev)
+    recs = {}
+    for kind, stage, src, nbytes in (
+            ("seq_to_head", 0, x, x.numel() * 2), ("seq_to_head", 1, None, x.numel() * 2),
+            ("head_to_seq", 0, None, x.numel() * 2), ("head_to_seq", 1, None, x.numel() * 2),
+            ("lse_gather", 0, lx, lx.numel() * 4), ("lse_gather", 1, None, lx.numel() * 4),
+            ("lse_scatter", 0, None, lx.numel() * 4), ("lse_scatter", 1, None, lx.numel() * 4)):
+        if src is None:
+            src = prev
+        D_ = D if not kind.startswith("lse") else 1
+        o_ = e3.ulysses(kind, stage, src, uly, B, Sl, H, D_)
+        t = _median_us(lambda: e3.ulysses(kind, stage, src, uly, B, Sl, H, D_, out=o_))
+        recs[f"{kind}/{stage}"] = {"us": round(t, 2), "roofline": _roof("hbm", 2 * nbytes, t)}
+        prev = o_
+    tot_b = 2 * (4 * x.numel() * 2 + 4 * lx.numel() * 4)
+    tot_t = sum(r["us"] for r in recs.values())
+    emit({"extra": "ulysses_transforms", "metric": "re-sharding GB/s (read + write)",
+          "value": round(tot_b / (tot_t * 1e-6) / 1e9, 1), "unit": "GB/s",
+          "roofline": _roof("hbm", tot_b, tot_t), "pieces": recs,
+          "config": {"workload": "ulysses_shard", "B": B, "S_local": Sl, "S_full": Sl * uly, "H": H, "D": D,
+                     "uly": uly},
+          "dtype": "bf16", "data": "synthetic (seeded N(0,1) inputs, resident in HBM)"})
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -189,6 +347,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of CPU oracle work for the baseline (0 = skip)")
     ap.add_argument("--no-flush", action="store_true")
+    ap.add_argument("--extras", action="store_true",
+                    help="instead of the headline: time the ring-step mode, the frozen-target "
+                         "forward and the Ulysses transforms (one JSON line each)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB before timing (a known-size "
                          "kernel for calibrating the HBM byte counters)")
@@ -210,12 +371,20 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.extras:
+        run_extras(args, dev)
+        return
     w = synth.workload(args.workload, seed=args.seed)
     log(f"[bench] workload {w}")
-    inp_cpu = synth.make_inputs(w)
-    d = {k: v.to(dev) for k, v in inp_cpu.items()}
     prob = e3.Problem(w.B, w.T, w.T_kv, w.H, w.D, w.num_blocks, w.scale, dtype=w.torch_dtype,
                       layout=w.layout, cp=w.cp, rank=w.rank, cu_seqlens=w.cu_seqlens(), device=dev)
+    if w.layout == "zigzag" and w.doc_lens is not None and len(w.doc_lens) > 1:
+        # a zig-zag share of several documents: its rows of the virtual global
+        # tensors, at the positions the library's layout tables give
+        inp_cpu = synth.make_inputs(w, positions=prob.query_positions())
+    else:
+        inp_cpu = synth.make_inputs(w)
+    d = {k: v.to(dev) for k, v in inp_cpu.items()}
     P0 = prob.pair_count()                      # per (batch row, head)
     out = torch.empty_like(d["q"])
     lse = torch.empty(w.B, w.H, w.T, dtype=torch.float32, device=dev)

@@ -127,6 +127,11 @@ def workload(name: str, seed: int = 0) -> Workload:
     if name == "zigzag":
         return Workload("zigzag", "bf16", 1, 131072, 32, 128, 8, layout="zigzag",
                         cp=8, rank=3, seed=seed)
+    if name == "zigzag_docs":
+        # the zig-zag share of a packed batch: eight 16384-token documents, each cut
+        # into 2cp chunks (measurement only; not one of the parity workloads)
+        return Workload("zigzag_docs", "bf16", 1, 131072, 32, 128, 8, layout="zigzag",
+                        cp=8, rank=3, doc_lens=[16384] * 8, seed=seed)
     raise KeyError(name)
 
 

@@ -35,6 +35,9 @@ CASES = {
                          doc_lens=[8, 400, 0, 616]),
     "zigzag_f32": W(dtype="f32", S=480, H=2, D=64, num_blocks=3, layout="zigzag", cp=3, rank=0,
                     doc_lens=[60, 6, 414]),
+    "zigzag_d64": W(S=512, H=2, D=64, num_blocks=3, layout="zigzag", cp=2, rank=0),
+    # no diagonal blocks: the diagonal kernel only turns the float32 dq into q's dtype
+    "contig_nb1": W(S=512, H=3, D=128, num_blocks=1, layout="contiguous", cp=2, rank=1, chunk=256),
 }
 
 

@@ -131,7 +131,7 @@ def workload(name: str, seed: int = 0) -> Workload:
         # the zig-zag share of a packed batch: eight 16384-token documents, each cut
         # into 2cp chunks (measurement only; not one of the parity workloads)
         return Workload("zigzag_docs", "bf16", 1, 131072, 32, 128, 8, layout="zigzag",
-                        cp=8, rank=3, doc_lens=[16384] * 8, seed=seed)
+                        cp=8, rank=3, doc_lens=[16384] * 8, seed=seed, chunk=1024)
     raise KeyError(name)
 
 
@@ -212,8 +212,12 @@ def make_inputs(w: Workload, device="cpu", with_dout: bool = True,
         loc = local_chunks(w, cp, rank, layout)
         pick = lambda t: t
     else:
-        loc = allc
-        idx = torch.as_tensor(np.asarray(positions, dtype=np.int64))
+        # only the generator chunks that hold the requested rows
+        ch = w.gen_chunk()
+        pos = np.asarray(positions, dtype=np.int64)
+        loc = sorted(set((pos // ch).tolist()))
+        slot = {c: i for i, c in enumerate(loc)}
+        idx = torch.as_tensor(np.array([slot[int(p) // ch] * ch + int(p) % ch for p in pos], dtype=np.int64))
         pick = lambda t: t.index_select(0, idx)
     out = {}
 

@@ -9,7 +9,9 @@ outputs (out, lse, dq, dkd, dvd) are compared on a sample of rows (the starts,
 middles and ends of both chunks, the rows around query-tile edges and seeded
 random rows), whose oracle values need only those rows' score rows. All heads
 are also checked for the properties that hold at any size (finite outputs, exact
-zeros for the K/V rows no local query sees, the softmax bounds of lse)."""
+zeros for the K/V rows no local query sees, the softmax bounds of lse). The
+zig-zag share of eight documents that the benchmark also times gets the same
+row-sample comparison and property checks."""
 import math
 
 import numpy as np
@@ -19,6 +21,7 @@ import torch
 import oracle
 import synth
 from tests.parity import TOL, assert_within, compare, rel, run_hip, run_oracle, say, stored_out
+from tests.parity import inputs as tinputs
 
 pytestmark = pytest.mark.gpu
 
@@ -71,17 +74,27 @@ def test_workload_parity_full_size(name, heads):
     inp_cache.clear()
 
 
+def share_runs(w):
+    """Lengths of the share's local runs in local order: the two zig-zag chunks of
+    every document (doc_len / 2cp rows each), else the whole share."""
+    if w.layout != "zigzag":
+        return [w.T]
+    docs = w.doc_lens if w.doc_lens is not None else [w.S]
+    return [n // (2 * w.cp) for n in docs for _ in range(2)]
+
+
 def sample_rows(w, n_random=16, seed=0):
     """Row sample of a share: the first, middle and last rows of each run (the
     zig-zag chunks), the rows on both sides of 64- and 128-row tile edges, and
     seeded random rows."""
-    c = w.T // 2 if w.layout == "zigzag" else w.T
     rows = set()
-    for r0 in range(0, w.T, c):
+    r0 = 0
+    for c in share_runs(w):
         for o in (0, 1, 2, 63, 64, 127, 128, 129, c // 2 - 1, c // 2, c - 129, c - 128, c - 65,
                   c - 64, c - 2, c - 1):
             if 0 <= o < c:
                 rows.add(r0 + o)
+        r0 += c
     rng = np.random.default_rng(seed)
     rows.update(int(x) for x in rng.integers(0, w.T, n_random))
     return np.array(sorted(rows))
@@ -108,15 +121,33 @@ def oracle_rows(w, inp, rows):
 
 
 @pytest.mark.timeout(900)
-def test_zigzag_share_all_heads_on_sampled_rows():
-    w = synth.workload("zigzag")
-    say(f"[workload] zigzag row sample: generating inputs {w}")
-    inp = synth.make_inputs(w)
-    say("[workload] zigzag row sample: HIP forward + backward")
+@pytest.mark.parametrize("name", ["zigzag", "zigzag_docs"])
+def test_zigzag_share_all_heads_on_sampled_rows(name):
+    """zigzag: one 131072-token document; zigzag_docs: eight 16384-token documents,
+    each cut into 2cp chunks (the bench's multi-document share). For the latter all
+    heads are also checked for the properties that hold at any size."""
+    w = synth.workload(name)
+    say(f"[workload] {name} row sample: generating inputs {w}")
+    inp = tinputs(w)
+    say(f"[workload] {name} row sample: HIP forward + backward")
     out, lse, (dq, dk0, dv0, dkd, dvd) = run_hip(w, inp)
+    if w.doc_lens is not None:
+        for nm, x in (("out", out), ("lse", lse), ("dq", dq), ("dk0", dk0), ("dv0", dv0), ("dkd", dkd),
+                      ("dvd", dvd)):
+            assert torch.isfinite(x.float()).all(), nm
+        cu = w.cu_seqlens()
+        qpos = oracle.query_positions(w.layout, w.T, w.cp, w.rank, cu)
+        seen = np.zeros(w.T_kv, dtype=bool)
+        for lo, hi in zip(cu[:-1], cu[1:]):
+            mine = qpos[(qpos >= lo) & (qpos < hi)]
+            if len(mine):
+                seen[lo:mine.max() + 1] = True
+        unseen = torch.from_numpy(np.nonzero(~seen)[0])
+        assert len(unseen) > 0
+        assert torch.count_nonzero(dk0[:, unseen]) == 0 and torch.count_nonzero(dv0[:, unseen]) == 0
     del dk0, dv0
     rows = torch.from_numpy(sample_rows(w))
-    say(f"[workload] zigzag row sample: oracle on {len(rows)} rows x {w.H} heads")
+    say(f"[workload] {name} row sample: oracle on {len(rows)} rows x {w.H} heads")
     ref = oracle_rows(w, inp, rows)
     t = TOL[w.dtype]
     f = lambda x: x.double().numpy()
@@ -127,7 +158,7 @@ def test_zigzag_share_all_heads_on_sampled_rows():
         m["dq"] = max(m["dq"], rel(f(dq[0, rows, h]), ref["dq"][h]))
         m["dkd"] = max(m["dkd"], rel(f(dkd[0][:, rows][:, :, h]), ref["dkd"][h]))
         m["dvd"] = max(m["dvd"], rel(f(dvd[0][:, rows][:, :, h]), ref["dvd"][h]))
-    say(f"[workload] zigzag row sample (worst head): {m}")
+    say(f"[workload] {name} row sample (worst head): {m}")
     assert m["out"] <= t["out"] and m["lse"] <= t["lse"], m
     for k in ("dq", "dkd", "dvd"):
         assert m[k] <= t["grad"], (k, m)

@@ -31,14 +31,15 @@
  *     `cached_ulysses_attention`); all merging is done in float32.
  *   - Every pointer passed to a compute entry point is a DEVICE pointer unless named
  *     *_host. The caller owns (allocates and frees) every buffer, including the
- *     backward's workspace. The library allocates no device memory and keeps no
- *     per-call state.
+ *     backward's workspace. The library allocates no device memory at run time and
+ *     keeps no per-call state (the only device memory it holds is the static scratch
+ *     array of eagle3_bwd_noalloc, part of its code object).
  *   - Calls are asynchronous on the given HIP stream and never synchronise. The backward
  *     forks part of its work (the diagonal-block gradients) onto a side stream that
  *     waits for the given stream and is joined back into it before the call's last
  *     kernel, so the result is ordered on the given stream as if all ran there. The side
- *     stream and its two events are created on first use, one set per host thread and
- *     device, and kept until the process ends.
+ *     stream and its fork and join events are created on first use, one set per host
+ *     thread and device, and kept until the process ends.
  *   - Every output is overwritten; rows of dk0/dv0 that no local query sees are written
  *     as zeros.
  *   - Errors: arguments are validated before anything is launched. On failure a negative

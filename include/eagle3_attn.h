@@ -247,8 +247,8 @@ int eagle3_ring_bwd_step(const e3_problem* p, int step, const void* dout, const 
 
 /* Closed-form diagonal gradients against the merged out/lse, and the final dq:
  * dkd, dvd [B,N,T,H,D] (dtype) and dq [B,T,H,D] (dtype) = dq_acc + scale * sum_i ds_i kd_i
- * (ring_attention page, `_CachedRingAttention`: "diagonal grads are added in closed
- * form"). With num_blocks == 1 it converts dq_acc to dq. No workspace. */
+ * (ring_attention page, `_CachedRingAttention`: the diagonal blocks' gradients follow in
+ * closed form). With num_blocks == 1 it converts dq_acc to dq. No workspace. */
 int eagle3_diag_bwd(const e3_problem* p, const void* dout, const void* q, const void* kd, const void* vd,
                     const void* out, const float* lse, const float* dq_acc, void* dq, void* dkd, void* dvd,
                     hipStream_t stream);

@@ -1,6 +1,6 @@
 // EAGLE-3 mixed attention, backward (gfx950).
 //
-// The backward runs against the MERGED joint-softmax out/lse (ring_attention page,
+// The backward takes the out/lse of the WHOLE joint softmax (ring_attention page,
 // `_CachedRingAttention`; ulysses_attention page, `_block0_backward`;
 // zigzag_ring_attention page, `zigzag_ring_flash_attn_varlen_backward`), so block-0
 // probabilities are P = exp(scale*q.k - lse) with the lse that includes the diagonal

@@ -10,7 +10,7 @@
  *     s <= pos(t) (causal, self included), score scale*<q_t, k0_s>, value v0_s;
  *   - blocks i = 1..N (N = num_blocks-1, the test-time-training steps): one key per
  *     row at the same position, score scale*<q_t, kd_{i,t}>, value vd_{i,t}.
- * The blocks are joined by the online-softmax log-sum-exp merge (ring_attention page,
+ * The blocks are joined by merging their log-sum-exps online (ring_attention page,
  * `_update_out_and_lse`, `_merge_diag`). The backward runs against the MERGED out/lse
  * (ring_attention page, `_CachedRingAttention`; zigzag_ring_attention page,
  * `zigzag_ring_flash_attn_varlen_backward`) and adds the diagonal gradients in closed
@@ -193,7 +193,7 @@ int lse_merge(float* out, float* lse, const float* block_out, const float* block
  *
  * The frozen target model's forward under context parallelism (target_cp page,
  * `attach_cp_kv_gather_hooks`): K/V are all-gathered across the cp group and each rank
- * attends its contiguous local queries against the full K/V with a global causal mask
+ * runs its contiguous local queries over the gathered K/V, masked causally by global position
  * (the O(S^2) scores stay sharded [S/cp, S]); tensors are head-major [B, nH, S, D] at
  * the attention call; forward only. This is the CONTIGUOUS share (or FULL) with
  * num_blocks == 1 in head-major layout:
@@ -256,7 +256,7 @@ int eagle3_diag_bwd(const e3_problem* p, const void* dout, const void* q, const 
 /* ---- Ulysses re-sharding: the local halves around the all-to-all ----------------------
  *
  * The Ulysses path (ulysses_attention page, module text and `_CachedUlyssesAttention`)
- * turns a sequence shard into a head shard with one all-to-all, runs block 0 over the
+ * re-shards from sequence to heads with one all-to-all, runs block 0 over the
  * full sequence for H/uly heads (the HEADSHARD layout above), sends out and lse back
  * with a second all-to-all and merges the diagonals on the sequence shard.
  * `_all_to_all_single` exchanges equal splits along dim 0: a send buffer is

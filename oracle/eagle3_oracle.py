@@ -26,10 +26,10 @@ class `_CachedRingAttention`; ...eagle.ulysses_attention, class
     dq_t  = scale (sum_s dS_{t,s} k0_s + sum_i ds_{t,i} kd_{i,t})
     dk0_s = scale sum_t dS_{t,s} q_t,   dv0_s = sum_t p_{t,s} dO_t
     dkd_{i,t} = scale ds_{t,i} q_t,     dvd_{i,t} = pi_{t,i} dO_t
-  (ring_attention page, `_CachedRingAttention`: the block-0 backward reuses the
-  merged out/lse and the diagonal gradients are added in closed form;
-  zigzag_ring_attention page, `zigzag_ring_flash_attn_varlen_backward`: each
-  block's backward sees the final merged out/lse.)
+  (ring_attention page, `_CachedRingAttention`: block 0's gradient is taken with
+  the out/lse of all blocks together, and the diagonal terms have a closed form;
+  zigzag_ring_attention page, `zigzag_ring_flash_attn_varlen_backward`: every
+  block's backward is given that final out/lse.)
 
 Everything is float64. The score rows are materialised explicitly, a block of
 rows at a time (rows are independent, so the grouping is only for memory); the
@@ -57,10 +57,10 @@ def query_positions(layout: str, T: int, cp: int = 1, rank: int = 0, cu_seqlens=
     """Global sequence position of each local query row.
 
     full / headshard: the whole sequence is local (ulysses_attention page,
-      module text: after the all-to-all a rank holds the full sequence for a
-      subset of heads).
+      module text: once the all-to-all has run, every rank has all positions,
+      for H/uly of the heads).
     contiguous: rank r holds positions [r*T, (r+1)*T) (ring_attention page,
-      module text: each rank holds a contiguous shard S/cp).
+      module text: the r-th run of S/cp consecutive positions).
     zigzag: every document is cut into 2*cp chunks; rank r holds chunk r
       (early) then chunk 2*cp-1-r (late) of each document, documents one after
       the other (zigzag_ring_attention page, module text: the 2*cp chunks and
@@ -224,8 +224,8 @@ def backward_head(dout, q, k0, v0, kd, vd, scale, qpos, cu_seqlens=None, out=Non
                   lse=None, rows=256):
     """Gradient of sum(out * dout) for one (batch row, head).
 
-    `out`/`lse` default to this oracle's own forward (the merged joint-softmax
-    out/lse). Passing another lse (e.g. the block-0-only lse) reproduces the
+    `out`/`lse` default to this oracle's own forward (out and lse of the joint
+    softmax over all blocks). Passing another lse (e.g. the block-0-only lse) reproduces the
     backward that the zigzag_ring_attention page warns against.
     Returns dq [T,D], dk0 [T_kv,D], dv0 [T_kv,D], dkd [N,T,D], dvd [N,T,D].
     """
@@ -339,7 +339,7 @@ def _sigmoid(x):
 
 
 def lse_merge(out, lse, block_out, block_lse):
-    """Online-softmax merge of a block (block_out, block_lse) into (out, lse),
+    """Folds one block's (block_out, block_lse) into the running (out, lse),
     in the sigmoid form of the ring_attention page (`_update_out_and_lse`,
     `_merge_diag`) and the zigzag_ring_attention page (`update_out_and_lse`):
         out' = out - sigmoid(block_lse - lse) * (out - block_out)

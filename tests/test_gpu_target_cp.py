@@ -1,6 +1,6 @@
 """GPU parity of the frozen-target context-parallel forward (target_cp page,
 `attach_cp_kv_gather_hooks`): a rank's contiguous local queries against the
-all-gathered K/V with a global causal mask, head-major [B, nH, S, D] tensors,
+all-gathered K/V, masked causally by global position, head-major [B, nH, S, D] tensors,
 forward only. It is the contiguous share with num_blocks = 1, so it is compared
 with the oracle's forward of that share, and with the token-major shard
 forward of the library (the same kernel over other strides: bitwise equal)."""

@@ -442,27 +442,27 @@ def test_zigzag_several_documents_equal_work_and_halves(cp, doc_lens):
 
 @pytest.mark.parametrize("cp,L", [(2, 4), (8, 16), (8, 1024)])
 def test_contiguous_last_rank_does_about_twice_the_mean(cp, L):
-    # ring_attention page, `_CachedZigZagRingAttention`: a contiguous shard
-    # leaves the last rank with about twice the work. Rank r: r*L^2 + L(L+1)/2.
+    # ring_attention page, `_CachedZigZagRingAttention`: with contiguous shards the
+    # last rank carries close to double the mean load. Rank r: r*L^2 + L(L+1)/2.
     counts = [oracle.pair_count("contiguous", L, cp, r) for r in range(cp)]
     assert counts == [r * L * L + L * (L + 1) // 2 for r in range(cp)]
     S = cp * L
     assert sum(counts) == S * (S + 1) // 2
     ratio = counts[-1] / (sum(counts) / cp)
-    assert 1.0 < ratio < 2.0                      # "about twice"; tends to 2 - 1/cp
+    assert 1.0 < ratio < 2.0                      # close to double; tends to 2 - 1/cp
     assert abs(ratio - (2.0 - 1.0 / cp)) < 1.0 / L
     if L >= 1024 and cp == 8:
         assert abs(ratio - 1.875) < 2e-3
 
 
 def test_ring_order_and_per_step_visibility():
-    # zigzag_ring_attention page, `RingComm`: send to rank+1, receive from
-    # rank-1, so step j holds rank (r-j) mod cp's K/V.
+    # zigzag_ring_attention page, `RingComm`: each step K/V move one rank up the
+    # ring, so step j holds rank (r-j) mod cp's K/V.
     steps = oracle.ring_steps("zigzag", 8, 3)
     assert [s for s, _ in steps] == [3, 2, 1, 0, 7, 6, 5, 4]
     assert steps[4][1] == [7, 8]
-    # ring_attention page, `ring_flash_attn_forward`: causal contiguous ring
-    # attends only blocks from itself and earlier ranks.
+    # ring_attention page, `ring_flash_attn_forward`: a causal contiguous share
+    # skips the K/V of higher ranks.
     assert [s for s, _ in oracle.ring_steps("contiguous", 4, 2)] == [2, 1, 0]
     # per-step visibility of the zig-zag share (early half = rows [0,c), late = [c,2c))
     cp, r, c = 4, 1, 4
@@ -480,8 +480,9 @@ def test_ring_order_and_per_step_visibility():
             assert front.all() and not back.any()
         else:            # only the late rows see the block, all of it
             assert not early.any() and late.all()
-    # the same rule inside every document of a packed sequence ("front/back half
-    # uses the halved cu_seqlens": zigzag_ring_attention page, `_block_forward`)
+    # the same rule inside every document of a packed sequence (the early and late
+    # halves of each document, addressed with cu_seqlens divided by two:
+    # zigzag_ring_attention page, `_block_forward`)
     doc_lens = [16, 32, 8]
     cu = np.concatenate([[0], np.cumsum(doc_lens)]).astype(np.int32)
     S = int(cu[-1])

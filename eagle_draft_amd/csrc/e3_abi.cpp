@@ -679,6 +679,9 @@ int eagle3_ulysses_seq_to_head(int stage, int dtype, int B, int S_local, int H, 
   const int es = esize(dtype);
   int rc = ulysses_check(what, stage, es, B, S_local, H, D, uly, src, dst);
   if (rc) return rc;
+  if (((long long)(H / uly) * D * es) % 4 != 0)   // segments are moved in 4-byte words
+    return fail(E3_EUNSUPPORTED, "%s: a segment of H/uly*D = %lld elements is not a multiple of 4 bytes", what,
+                (long long)(H / uly) * D);
   if (S_local == 0) return ok();
   const long long Hl = H / uly, HD = (long long)H * D, RL = Hl * D, Sl = S_local, Sf = (long long)uly * Sl;
   e3::SegCopy c{static_cast<const char*>(src), static_cast<char*>(dst), 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
@@ -705,6 +708,9 @@ int eagle3_ulysses_head_to_seq(int stage, int dtype, int B, int S_local, int H, 
   const int es = esize(dtype);
   int rc = ulysses_check(what, stage, es, B, S_local, H, D, uly, src, dst);
   if (rc) return rc;
+  if (((long long)(H / uly) * D * es) % 4 != 0)   // segments are moved in 4-byte words
+    return fail(E3_EUNSUPPORTED, "%s: a segment of H/uly*D = %lld elements is not a multiple of 4 bytes", what,
+                (long long)(H / uly) * D);
   if (S_local == 0) return ok();
   const long long Hl = H / uly, HD = (long long)H * D, RL = Hl * D, Sl = S_local, Sf = (long long)uly * Sl;
   e3::SegCopy c{static_cast<const char*>(src), static_cast<char*>(dst), 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};

@@ -266,7 +266,9 @@ int eagle3_diag_bwd(const e3_problem* p, const void* dout, const void* q, const 
  * src into the send buffer dst, stage 1 unpacks the receive buffer src into dst.
  * H is the GLOBAL head count and must divide by uly; S_full = uly * S_local. dtype is
  * E3_BF16 or E3_F32; lse is float32. src and dst are device buffers, 4-byte aligned,
- * not the same buffer; results are exact copies.
+ * not the same buffer; results are exact copies. Data moves in 4-byte words: a head
+ * group's row of H/uly*D elements must be a multiple of 4 bytes (with E3_BF16,
+ * H/uly*D even), else E3_EUNSUPPORTED.
  *
  * `_gather_seq_scatter_heads`: x [B, S_local, H, D] -> [B, S_full, H/uly, D]
  *   stage 0: x -> send [uly][B][S_local][H/uly][D] (head group g to rank g)

@@ -282,3 +282,18 @@ def test_noalloc_backward_refuses_a_problem_larger_than_its_scratch():
     a = ctypes.c_void_p(0x1000)        # never dereferenced: the size check fails first
     rc = lib.eagle3_bwd_noalloc(p.ref(), *([a] * 13), None)
     assert rc == e3.E3_EINVAL and "scratch" in lib.eagle3_last_error().decode()
+
+
+def test_ulysses_transforms_refuse_segments_that_are_not_whole_words():
+    """The re-sharding copies move 4-byte words: a bf16 head-group row of an odd
+    number of elements is refused (nothing is launched), float32 is accepted up to
+    the launch and an even bf16 row passes validation too."""
+    lib = e3.lib()
+    a, b = ctypes.c_void_p(0x1000), ctypes.c_void_p(0x2000)   # never dereferenced here
+    for name in ("eagle3_ulysses_seq_to_head", "eagle3_ulysses_head_to_seq"):
+        f = getattr(lib, name)
+        for stage in (0, 1):
+            rc = f(stage, e3.DTYPES[torch.bfloat16], 1, 5, 2, 3, 2, a, b, None)   # H/uly*D = 3
+            assert rc == e3.E3_EUNSUPPORTED and "multiple of 4 bytes" in lib.eagle3_last_error().decode()
+            rc = f(stage, e3.DTYPES[torch.bfloat16], 1, 0, 2, 4, 2, a, b, None)   # S_local = 0: nothing to do
+            assert rc == e3.E3_OK

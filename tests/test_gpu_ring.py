@@ -11,8 +11,12 @@
   * the backward run step by step for EVERY rank of the ring, with the K/V
     gradients of each step added into accumulators that stand for the rotated
     dK/dV buffers, gives each rank's dq, dkd, dvd and, summed over ranks, the
-    full-sequence dk0, dv0 of the oracle."""
+    full-sequence dk0, dv0 of the oracle;
+
+on fixed shares and on seeded random ones (layout, degree, rank, documents,
+num_blocks, head dim, dtype)."""
 import dataclasses
+import random
 
 import numpy as np
 import pytest
@@ -39,6 +43,36 @@ CASES = {
     # no diagonal blocks: the diagonal kernel only turns the float32 dq into q's dtype
     "contig_nb1": W(S=512, H=3, D=128, num_blocks=1, layout="contiguous", cp=2, rank=1, chunk=256),
 }
+
+
+def ring_fuzz_case(i):
+    """Seeded random ring shares: contiguous (random documents) or zig-zag (documents
+    whose lengths are multiples of 2cp), cp 2..4, any rank, num_blocks 1..5, both
+    head dims and dtypes, lengths that match no tile size."""
+    rng = random.Random(7000 + i)
+    dtype = "f32" if i % 4 == 3 else "bf16"
+    D = rng.choice([64, 128])
+    cp = rng.randint(2, 4)
+    kw = dict(dtype=dtype, D=D, H=rng.randint(1, 3), num_blocks=rng.randint(1, 5), seed=100 + i, cp=cp,
+              rank=rng.randrange(cp))
+    if i % 2 == 0:
+        t = rng.randint(33, 260)
+        S = cp * t
+        docs = None
+        if rng.random() < 0.6:
+            docs, acc = [], 0
+            while acc < S:
+                n = min(rng.choice([0, 1, rng.randint(2, 90), rng.randint(60, 500)]), S - acc)
+                docs.append(n)
+                acc += n
+        return W(S=S, layout="contiguous", chunk=t, doc_lens=docs, **kw)
+    docs = [2 * cp * rng.choice([0, 1, rng.randint(2, 12), rng.randint(10, 60)]) for _ in range(rng.randint(1, 4))]
+    if sum(docs) == 0:
+        docs[0] = 2 * cp
+    return W(S=sum(docs), layout="zigzag", doc_lens=docs if len(docs) > 1 else None, **kw)
+
+
+CASES.update({f"fuzz{i}": ring_fuzz_case(i) for i in range(8)})
 
 
 def step_keys(w, step):

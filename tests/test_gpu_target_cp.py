@@ -4,6 +4,8 @@ all-gathered K/V, masked causally by global position, head-major [B, nH, S, D] t
 forward only. It is the contiguous share with num_blocks = 1, so it is compared
 with the oracle's forward of that share, and with the token-major shard
 forward of the library (the same kernel over other strides: bitwise equal)."""
+import random
+
 import numpy as np
 import pytest
 import torch
@@ -25,6 +27,28 @@ CASES = {
     "cp2_b2_d64": W(B=2, S=600, H=2, D=64, num_blocks=1, layout="contiguous", cp=2, rank=1, chunk=300),
     "f32_cp4": W(dtype="f32", S=512, H=2, D=64, num_blocks=1, layout="contiguous", cp=4, rank=2, chunk=128),
 }
+
+
+def _fuzz(i):
+    """Seeded random contiguous shares: degree, rank, batch rows or documents,
+    head dim, dtype, lengths that match no tile size."""
+    rng = random.Random(8000 + i)
+    cp = rng.randint(1, 5)
+    t = rng.randint(1, 300)
+    S = cp * t
+    kw = dict(dtype="f32" if i % 3 == 2 else "bf16", D=rng.choice([64, 128]), H=rng.randint(1, 3), num_blocks=1,
+              seed=200 + i, layout="contiguous", cp=cp, rank=rng.randrange(cp), chunk=t)
+    if rng.random() < 0.5:
+        docs, acc = [], 0
+        while acc < S:
+            n = min(rng.choice([0, 1, rng.randint(2, 120), rng.randint(100, 600)]), S - acc)
+            docs.append(n)
+            acc += n
+        return W(S=S, doc_lens=docs, **kw)
+    return W(S=S, B=rng.randint(1, 2), **kw)
+
+
+CASES.update({f"fuzz{i}": _fuzz(i) for i in range(6)})
 
 
 @pytest.mark.parametrize("name", list(CASES))

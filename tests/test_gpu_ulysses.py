@@ -10,6 +10,8 @@ rank i's receive buffer):
     shards, block 0 over the full sequence on the head shard, out and lse back
     to the sequence shard, the diagonal blocks merged there; backward likewise
     with the merged out/lse -- equals the oracle's joint softmax and gradients."""
+import random
+
 import numpy as np
 import pytest
 import torch
@@ -29,10 +31,27 @@ def a2a(sends):
     return [torch.stack([sends[i][r] for i in range(uly)], 0).contiguous() for r in range(uly)]
 
 
+def _random_shapes(n):
+    """Seeded random transform shapes: odd lengths, head counts that divide by the
+    degree, and head dims whose rows are not 16-byte multiples (the 4-byte copies)."""
+    rng = random.Random(9000)
+    out = []
+    for _ in range(n):
+        uly = rng.randint(1, 8)
+        out.append((rng.randint(1, 2), rng.randint(1, 97), uly * rng.randint(1, 4), rng.choice([2, 6, 64, 128]),
+                    uly))
+    return out + [(1, 9, 6, 3, 2)]       # a row of 3 elements: float32 copies it, bf16 is refused
+
+
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("B,S_local,H,D,uly", [(1, 64, 8, 128, 4), (2, 37, 6, 64, 3), (1, 5, 4, 128, 1),
-                                               (1, 130, 16, 128, 8)])
+                                               (1, 130, 16, 128, 8)] + _random_shapes(6))
 def test_transforms_are_exact_and_invert(dtype, B, S_local, H, D, uly):
+    if dtype == torch.bfloat16 and (H // uly * D) % 2:
+        x = torch.zeros(B, S_local, H, D, dtype=dtype, device="cuda")
+        with pytest.raises(e3.E3Error, match="multiple of 4 bytes"):
+            e3.ulysses("seq_to_head", 0, x, uly, B, S_local, H, D)
+        return
     g = torch.Generator().manual_seed(B * 1000 + S_local)
     Sf, Hl = uly * S_local, H // uly
     X = torch.randn(B, Sf, H, D, generator=g).to(dtype).cuda()

@@ -3,7 +3,9 @@ allocate device memory) against the backward with a workspace whose kernels it
 shares (eagle3_shard_bwd): two calls in a row,
 the second with a smaller input, each compared at the parity tolerances; the
 K/V and diagonal gradients come from the same kernels and must be bitwise equal,
-dq differs only by the rounding of its block-0 part to q's dtype."""
+dq differs only by the rounding of its block-0 part to q's dtype. The same holds on
+a float32 contiguous share with documents, a multi-document zig-zag share at D = 64,
+a head shard and num_blocks = 12."""
 import pytest
 import torch
 
@@ -43,3 +45,22 @@ def test_noalloc_backward_matches_the_workspace_backward_twice():
         err = rel(got[0].double().cpu().numpy(), ref[0].double().cpu().numpy())
         say(f"[noalloc] dq relative difference {err:.3g}")
         assert err <= t["grad"]
+
+
+@pytest.mark.parametrize("w", [
+    W(dtype="f32", S=300, H=2, D=64, num_blocks=3, layout="contiguous", cp=3, rank=2, chunk=100,
+      doc_lens=[40, 1, 259], seed=5),
+    W(S=960, H=2, D=64, num_blocks=4, layout="zigzag", cp=2, rank=1, doc_lens=[260, 4, 696], seed=6),
+    W(S=768, H=3, D=128, num_blocks=5, layout="headshard", cp=4, doc_lens=[500, 268], seed=7),
+    W(S=200, H=2, D=128, num_blocks=12, seed=8),
+], ids=["f32_contig_docs", "zigzag_docs_d64", "headshard", "nb12"])
+def test_noalloc_backward_on_more_shares(w):
+    say(f"[noalloc] {w}")
+    ref, got = run_both(w)
+    t = TOL[w.dtype]
+    names = ("dq", "dk0", "dv0", "dkd", "dvd")
+    for n, b in zip(names, got):
+        assert torch.isfinite(b.float()).all(), n
+    for n, a, b in zip(names[1:], ref[1:], got[1:]):
+        assert torch.equal(a, b), n
+    assert rel(got[0].double().cpu().numpy(), ref[0].double().cpu().numpy()) <= t["grad"]

@@ -262,6 +262,8 @@ int bwd_impl(const e3_problem* p, const void* dout, const void* q, const void* k
   a.lse_in = lse;
   {
     const BwdWs l = bwd_ws_layout(p);
+    if (l.delta > 0xffffffffull)   // the kernels address delta from lse*log2(e) with a 32-bit offset
+      return fail(E3_EUNSUPPORTED, "B*H*P = %zu rows of delta do not fit a 32-bit byte offset", l.delta / 4);
     char* w = static_cast<char*>(ws);
     a.q_pitch = l.pitch;
     a.lse2 = reinterpret_cast<float*>(w);
@@ -600,6 +602,8 @@ int eagle3_ring_bwd_step(const e3_problem* p, int step, const void* dout, const 
   a.lse_in = lse;
   {
     const BwdWs l = bwd_ws_layout(p);
+    if (l.delta > 0xffffffffull)   // the kernels address delta from lse*log2(e) with a 32-bit offset
+      return fail(E3_EUNSUPPORTED, "B*H*P = %zu rows of delta do not fit a 32-bit byte offset", l.delta / 4);
     char* w = static_cast<char*>(workspace);
     a.q_pitch = l.pitch;
     a.lse2 = reinterpret_cast<float*>(w);

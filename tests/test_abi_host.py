@@ -297,3 +297,17 @@ def test_ulysses_transforms_refuse_segments_that_are_not_whole_words():
             assert rc == e3.E3_EUNSUPPORTED and "multiple of 4 bytes" in lib.eagle3_last_error().decode()
             rc = f(stage, e3.DTYPES[torch.bfloat16], 1, 0, 2, 4, 2, a, b, None)   # S_local = 0: nothing to do
             assert rc == e3.E3_OK
+
+
+def test_backward_refuses_a_delta_offset_beyond_32_bits():
+    """lse*log2(e) and delta sit B*H*P floats apart in the workspace and the kernels
+    address one from the other with a 32-bit byte offset: a larger problem is refused
+    before anything is launched."""
+    lib = e3.lib()
+    a = ctypes.c_void_p(0x1000)        # never dereferenced: the check fails first
+    T = 1 << 20
+    p = e3.Problem(1, T, T, 1100, 64, 1, 0.125, dtype=torch.bfloat16)      # 1100 * 2^20 * 4 B > 4 GiB
+    rc = lib.eagle3_attn_bwd(p.ref(), *([a] * 9), a, a, a, None, None, None)
+    assert rc == e3.E3_EUNSUPPORTED and "32-bit" in lib.eagle3_last_error().decode()
+    rc = lib.eagle3_ring_bwd_step(p.ref(), 0, *([a] * 10), None)
+    assert rc == e3.E3_EUNSUPPORTED and "32-bit" in lib.eagle3_last_error().decode()

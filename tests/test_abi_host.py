@@ -145,8 +145,7 @@ def share_problem(layout, T, cp, rank, cu):
                       rank=rank, cu_seqlens=cu)
 
 
-@pytest.mark.parametrize("layout,T,cp,rank,cu", SHARES)
-def test_shard_driver_positions_and_pair_counts(layout, T, cp, rank, cu):
+def check_positions_and_pairs(layout, T, cp, rank, cu):
     p = share_problem(layout, T, cp, rank, cu)
     pos = p.query_positions()
     ocp = cp if layout in ("contiguous", "zigzag") else 1
@@ -155,10 +154,19 @@ def test_shard_driver_positions_and_pair_counts(layout, T, cp, rank, cu):
 
 
 @pytest.mark.parametrize("layout,T,cp,rank,cu", SHARES)
+def test_shard_driver_positions_and_pair_counts(layout, T, cp, rank, cu):
+    check_positions_and_pairs(layout, T, cp, rank, cu)
+
+
+@pytest.mark.parametrize("layout,T,cp,rank,cu", SHARES)
 def test_shard_driver_key_tiles_cover_exactly_the_visible_keys(layout, T, cp, rank, cu):
     """Every query row counts each visible block-0 key exactly once over the
     key tiles the kernel visits; unmasked tiles are fully visible to every row
     of their query tile; the tiles of a segment follow the ring order."""
+    check_key_tile_coverage(layout, T, cp, rank, cu)
+
+
+def check_key_tile_coverage(layout, T, cp, rank, cu):
     p = share_problem(layout, T, cp, rank, cu)
     ocp = cp if layout in ("contiguous", "zigzag") else 1
     qpos = oracle.query_positions(layout, T, ocp, rank, cu)
@@ -211,6 +219,52 @@ def test_shard_driver_key_tiles_cover_exactly_the_visible_keys(layout, T, cp, ra
     if cu is None and layout != "zigzag":
         assert heavy == sorted(heavy, reverse=True)    # latest positions (most keys) launch first
 
+
+
+def random_share(i):
+    """Seeded random share (layout, local T, cp, rank, cu_seqlens) within what the
+    library accepts: any document list (empty documents included) for the full,
+    head-shard and contiguous layouts; documents of whole 2cp chunks (one-row chunks
+    and empty documents included) for the zig-zag layout."""
+    rng = np.random.default_rng(7000 + i)
+    layout = ("full", "headshard", "contiguous", "zigzag")[i % 4]
+    cp = 1 if layout == "full" else int(rng.integers(1, 9))
+    rank = int(rng.integers(0, cp))
+    nd = int(rng.integers(1, 7))
+    if layout == "zigzag":
+        # a quarter of the documents empty, a quarter of one-row chunks
+        kind = rng.integers(0, 4, size=nd)
+        lens = [0 if k == 0 else 2 * cp if k == 1 else 2 * cp * int(rng.integers(1, 200 // cp + 2))
+                for k in kind]
+        if sum(lens) == 0:
+            lens[0] = 2 * cp
+        S = sum(lens)
+        T = S // cp
+    else:
+        if layout == "full":
+            T = S = int(rng.integers(1, 1500))
+        elif layout == "headshard":
+            S = T = cp * int(rng.integers(1, 300))
+        else:
+            T = int(rng.integers(1, 400))
+            S = T * cp
+        cuts = rng.integers(0, S + 1, size=nd - 1)
+        if nd > 2:
+            cuts[1] = cuts[0]                      # an empty document
+        cuts = np.sort(cuts)
+        lens = np.diff(np.concatenate([[0], cuts, [S]])).tolist()
+    if nd == 1 and rng.random() < 0.5:
+        return layout, T, cp, rank, None
+    return layout, T, cp, rank, [0] + np.cumsum(lens).astype(int).tolist()
+
+
+@pytest.mark.parametrize("i", range(48))
+def test_shard_driver_on_seeded_random_shares(i):
+    """Positions, pair counts and key-tile coverage of 48 seeded random shares
+    (12 per layout) against the oracle: integer work, compared exactly."""
+    layout, T, cp, rank, cu = random_share(i)
+    check_positions_and_pairs(layout, T, cp, rank, cu)
+    check_key_tile_coverage(layout, T, cp, rank, cu)
 
 def test_workload_pair_counts_match_golden():
     import json

@@ -138,7 +138,10 @@ int eagle3_attn_fwd(const e3_problem* p, const void* q, const void* k0, const vo
 /* Backward of the full sequence (layout FULL or HEADSHARD) against the MERGED out/lse
  * produced by the forward: writes dq [B,T,H,D], dk0/dv0 [B,T_kv,H,D], dkd/dvd
  * [B,N,T,H,D] (dtype; dkd/dvd may be NULL when num_blocks == 1). workspace must hold
- * eagle3_bwd_workspace_bytes(p) bytes, 256-byte aligned. */
+ * eagle3_bwd_workspace_bytes(p) bytes, 256-byte aligned. The kernels address the
+ * workspace's delta rows with a 32-bit byte offset: problems with B*H*P >= 2^30 (P as for
+ * eagle3_bwd_workspace_bytes) are refused with E3_EUNSUPPORTED, here and in
+ * eagle3_shard_bwd and eagle3_ring_bwd_step. */
 int eagle3_attn_bwd(const e3_problem* p, const void* dout, const void* q, const void* k0,
                     const void* v0, const void* kd, const void* vd, const void* out,
                     const float* lse, void* workspace, void* dq, void* dk0, void* dv0,

@@ -39,7 +39,10 @@
  *     waits for the given stream and is joined back into it before the call's last
  *     kernel, so the result is ordered on the given stream as if all ran there. The side
  *     stream and its fork and join events are created on first use, one set per host
- *     thread and device, and kept until the process ends.
+ *     thread and device, and kept until the process ends. No call allocates, synchronises
+ *     or issues a memset, so the forward and backward can be captured in a HIP graph
+ *     (the side stream joins the capture through its events); make one eager backward
+ *     call on the capturing thread first, so that the side stream exists.
  *   - Every output is overwritten; rows of dk0/dv0 that no local query sees are written
  *     as zeros.
  *   - Errors: arguments are validated before anything is launched. On failure a negative

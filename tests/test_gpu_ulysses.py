@@ -45,7 +45,9 @@ def _random_shapes(n):
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("B,S_local,H,D,uly", [(1, 64, 8, 128, 4), (2, 37, 6, 64, 3), (1, 5, 4, 128, 1),
-                                               (1, 130, 16, 128, 8)] + _random_shapes(6))
+                                               (1, 130, 16, 128, 8),
+                                               (1, 4096, 32, 128, 8)]    # the size bench.py --extras times
+                         + _random_shapes(6))
 def test_transforms_are_exact_and_invert(dtype, B, S_local, H, D, uly):
     if dtype == torch.bfloat16 and (H // uly * D) % 2:
         x = torch.zeros(B, S_local, H, D, dtype=dtype, device="cuda")

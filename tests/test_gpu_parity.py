@@ -19,6 +19,7 @@ CASES = {
     "bf16_full_384": W(S=384, H=2, D=128, num_blocks=3),
     "bf16_full_ragged_1000": W(S=1000, H=3, D=128, num_blocks=4),
     "bf16_full_d64": W(S=520, H=2, D=64, num_blocks=3),
+    "bf16_long_d64_docs": W(S=3000, H=4, D=64, num_blocks=8, doc_lens=[1200, 1, 1799], seed=41),
     "bf16_nb1": W(S=400, H=2, D=128, num_blocks=1),
     "bf16_batch2": W(B=2, S=300, H=2, D=128, num_blocks=2),
     "bf16_varlen": W(S=1200, H=2, D=128, num_blocks=3, doc_lens=[1, 300, 0, 77, 500, 1, 321]),
